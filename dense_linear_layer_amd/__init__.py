@@ -1,0 +1,234 @@
+"""Python binding of the fused fp32 linear layer library (liblin_epi.so).
+
+The functions below carry the C names of ``include/lin_epi.h`` and only
+marshal arguments (ctypes); every step of the computation runs in the HIP
+kernels of the library.  PyTorch is used for device memory and streams only,
+in :class:`LinEpi`.  There is no CPU fallback: if the library is missing, the
+first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblin_epi.so")
+
+# lin_epi_kind
+LIN_EPI_NONE = 0
+LIN_EPI_SCALE_HARDTANH_GELU = 1
+LIN_EPI_POOL_GELU_SCALE_ROWMAX = 2
+LIN_EPI_SWISH_SCALE = 3
+
+# status codes
+LIN_EPI_OK = 0
+LIN_EPI_EINVAL = -1
+LIN_EPI_EALIGN = -2
+LIN_EPI_ENOTSUP = -3
+LIN_EPI_ENOMEM = -4
+LIN_EPI_EHIP = -5
+
+# options
+LIN_EPI_OPT_SPLIT_K = 1
+LIN_EPI_OPT_PROFILE = 2
+
+# every function include/lin_epi.h declares
+EXPORTS = (
+    "lin_epi_create",
+    "lin_epi_run",
+    "lin_epi_destroy",
+    "lin_epi_status_string",
+    "lin_epi_set_option",
+    "lin_epi_last_plan",
+    "lin_epi_profile_read",
+)
+
+
+class lin_epi_desc(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("ht_min", ctypes.c_float),
+        ("ht_max", ctypes.c_float),
+        ("pool_kernel", ctypes.c_int32),
+        ("pool_stride", ctypes.c_int32),
+    ]
+
+
+class lin_epi_plan(ctypes.Structure):
+    _fields_ = [
+        ("tile_m", ctypes.c_int32),
+        ("tile_n", ctypes.c_int32),
+        ("tile_k", ctypes.c_int32),
+        ("split_k", ctypes.c_int32),
+        ("grid_main", ctypes.c_int64),
+        ("kernels", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
+class lin_epi_profile(ctypes.Structure):
+    _fields_ = [
+        ("launches", ctypes.c_int64 * 2),
+        ("total_ms", ctypes.c_double * 2),
+    ]
+
+
+class LinEpiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (where, lin_epi_status_string(status), status))
+
+
+_lib = None
+
+
+def load_library():
+    """Load liblin_epi.so (built in-tree by dense_linear_layer_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("liblin_epi.so is not built (%s); run `python -m dense_linear_layer_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.lin_epi_create.argtypes = [ctypes.POINTER(p), p]
+    lib.lin_epi_create.restype = ctypes.c_int
+    lib.lin_epi_run.argtypes = [p, i64, i64, i64, p, p, p, ctypes.POINTER(lin_epi_desc), p]
+    lib.lin_epi_run.restype = ctypes.c_int
+    lib.lin_epi_destroy.argtypes = [p]
+    lib.lin_epi_destroy.restype = ctypes.c_int
+    lib.lin_epi_status_string.argtypes = [ctypes.c_int]
+    lib.lin_epi_status_string.restype = ctypes.c_char_p
+    lib.lin_epi_set_option.argtypes = [p, i32, i64]
+    lib.lin_epi_set_option.restype = ctypes.c_int
+    lib.lin_epi_last_plan.argtypes = [p, ctypes.POINTER(lin_epi_plan)]
+    lib.lin_epi_last_plan.restype = ctypes.c_int
+    lib.lin_epi_profile_read.argtypes = [p, ctypes.POINTER(lin_epi_profile)]
+    lib.lin_epi_profile_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---- the C entry points, same names, plain integers for pointers ----------
+
+def lin_epi_status_string(status: int) -> str:
+    return load_library().lin_epi_status_string(int(status)).decode()
+
+
+def lin_epi_create(hip_stream: int | None = None) -> tuple[int, int]:
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    rc = load_library().lin_epi_create(ctypes.byref(h), ctypes.c_void_p(hip_stream or None))
+    return rc, (h.value or 0)
+
+
+def lin_epi_run(handle: int, M: int, N: int, K: int, X: int, W: int, b: int, desc: lin_epi_desc | None,
+                Y: int) -> int:
+    d = ctypes.byref(desc) if desc is not None else None
+    return load_library().lin_epi_run(ctypes.c_void_p(handle or None), M, N, K, ctypes.c_void_p(X or None),
+                                      ctypes.c_void_p(W or None), ctypes.c_void_p(b or None), d,
+                                      ctypes.c_void_p(Y or None))
+
+
+def lin_epi_destroy(handle: int) -> int:
+    return load_library().lin_epi_destroy(ctypes.c_void_p(handle or None))
+
+
+def lin_epi_set_option(handle: int, option: int, value: int) -> int:
+    return load_library().lin_epi_set_option(ctypes.c_void_p(handle or None), option, value)
+
+
+def lin_epi_last_plan(handle: int) -> tuple[int, lin_epi_plan]:
+    p = lin_epi_plan()
+    rc = load_library().lin_epi_last_plan(ctypes.c_void_p(handle or None), ctypes.byref(p))
+    return rc, p
+
+
+def lin_epi_profile_read(handle: int) -> tuple[int, lin_epi_profile]:
+    p = lin_epi_profile()
+    rc = load_library().lin_epi_profile_read(ctypes.c_void_p(handle or None), ctypes.byref(p))
+    return rc, p
+
+
+def make_desc(kind: int, scale: float = 1.0, ht_min: float = -1.0, ht_max: float = 1.0, pool_kernel: int = 16,
+              pool_stride: int | None = None) -> lin_epi_desc:
+    return lin_epi_desc(int(kind), float(scale), float(ht_min), float(ht_max), int(pool_kernel),
+                        int(pool_kernel if pool_stride is None else pool_stride))
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != LIN_EPI_OK:
+        raise LinEpiError(rc, where)
+
+
+class LinEpi:
+    """A handle bound to a torch CUDA (HIP) stream; runs on torch tensors.
+
+    ``run(X, W, b, desc)`` allocates Y with torch (device memory only) and
+    calls lin_epi_run; the result is enqueued on the handle's stream.
+    """
+
+    def __init__(self, stream=None):
+        self.stream = stream
+        ptr = stream.cuda_stream if stream is not None else 0
+        rc, self.handle = lin_epi_create(ptr)
+        _check(rc, "lin_epi_create")
+
+    def close(self) -> None:
+        if self.handle:
+            rc = lin_epi_destroy(self.handle)
+            self.handle = 0
+            _check(rc, "lin_epi_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            if self.handle:
+                lin_epi_destroy(self.handle)
+                self.handle = 0
+        except Exception:
+            pass
+
+    def set_option(self, option: int, value: int) -> None:
+        _check(lin_epi_set_option(self.handle, option, value), "lin_epi_set_option")
+
+    def plan(self) -> lin_epi_plan:
+        rc, p = lin_epi_last_plan(self.handle)
+        _check(rc, "lin_epi_last_plan")
+        return p
+
+    def profile(self) -> lin_epi_profile:
+        rc, p = lin_epi_profile_read(self.handle)
+        _check(rc, "lin_epi_profile_read")
+        return p
+
+    @staticmethod
+    def output_shape(M: int, N: int, kind: int) -> tuple:
+        return (M,) if kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX else (M, N)
+
+    def run_into(self, X, W, b, desc: lin_epi_desc, Y) -> None:
+        M, K = X.shape
+        N = W.shape[0]
+        rc = lin_epi_run(self.handle, M, N, K, X.data_ptr(), W.data_ptr(), b.data_ptr(), desc, Y.data_ptr())
+        _check(rc, "lin_epi_run")
+
+    def run(self, X, W, b, desc: lin_epi_desc):
+        import torch
+
+        for name, t in (("X", X), ("W", W), ("b", b)):
+            if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous float32 device tensor" % name)
+        M, K = X.shape
+        N, K2 = W.shape
+        if K2 != K or tuple(b.shape) != (N,):
+            raise ValueError("shape mismatch: X %s, W %s, b %s" % (tuple(X.shape), tuple(W.shape), tuple(b.shape)))
+        Y = torch.empty(self.output_shape(M, N, desc.kind), dtype=torch.float32, device=X.device)
+        self.run_into(X, W, b, desc, Y)
+        return Y

@@ -1,0 +1,319 @@
+// MFMA-tiled fp32 GEMM with a fused epilogue, for gfx950 (CDNA4).
+//
+// Computes, for one BM x BN output tile per workgroup,
+//     acc[m, n] = sum_k X[m, k] * W[n, k]        (X [M,K], W [N,K], both K-contiguous)
+// with v_mfma_f32_32x32x2_f32 (fp32 products, fp32 accumulation), then
+// applies the bias and the tail in registers and stores the result once.
+// This is the "compute the GEMM tile into registers, apply the tail, write
+// the final output" plan that page "Kimi-K2.6 l2_p53" names as the ideal
+// fusion and page "Kimi-K2.6 l2_p59" sketches as a tiled kernel with staged
+// input/weight tiles and a register epilogue.
+//
+// Data flow per workgroup (NT = 64 * WAVES_M * WAVES_N threads):
+//   * global -> registers: 128-bit loads; eight consecutive threads read one
+//     BK=32-float (128-byte) row segment of X or W, so each wavefront load
+//     covers whole cache lines.  Rows past M/N and k past the slice end are
+//     zero-filled (K is a multiple of 4, so a float4 is all-in or all-out).
+//   * registers -> LDS: two stages (double buffer); row stride BK+4 floats,
+//     which makes both the 128-bit stores and the 128-bit fragment reads
+//     bank-conflict free.
+//   * LDS -> MFMA operands: the contraction index is permuted inside each
+//     group of 8 k: lane l of a 32x32x2 MFMA supplies k-slot l/32, and the
+//     four MFMAs of one group use components 0..3 of a float4 read at
+//     k = 8g + 4*(l/32).  A and B use the same permutation, so the sum over
+//     k is unchanged, and both operands come from K-contiguous 128-bit reads
+//     (no transpose of the [N,K] weight is ever needed).
+//
+// Accumulator layout of v_mfma_f32_32x32x2_f32 (one 32x32 block, 16 VGPRs):
+// lane l, register r holds C[row][col] with col = l % 32 and
+// row = 8*(r/4) + 4*(l/32) + r%4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "epilogue.hpp"
+
+namespace lin_epi {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+enum EpiKind : int {
+    EPI_NONE = 0,
+    EPI_SCALE_HARDTANH_GELU = 1,
+    EPI_POOL_GELU_SCALE_ROWMAX = 2,
+    EPI_SWISH_SCALE = 3,
+    EPI_SPLITK_PARTIAL = 4,  // raw partial sums of one K slice, no bias/tail
+};
+
+struct GemmArgs {
+    const float *X;
+    const float *W;
+    const float *bias;
+    float *out;       // Y [M,N]; or split-K slices [S,M,N]; or row-max partials [M, tiles_n]
+    int32_t M, N, K;
+    int32_t k_slice;  // K elements per split-K slice (multiple of BK); >= K when not split
+    int32_t tiles_m, tiles_n;
+    TailParams tail;
+};
+
+// Workgroup index -> output tile, XCD-aware.  Workgroups are dispatched
+// round-robin over the 8 XCDs (wg % 8), each XCD with its own L2.  The first
+// 8*q workgroups (q = tiles / 8) are renumbered so that XCD x owns the
+// contiguous tile range [x*q, (x+1)*q); the remainder keeps its index.  The
+// tile number is then unfolded GROUP_M tile-rows at a time (column-major
+// inside a group), so the workgroups resident on one XCD cover a compact
+// block of tiles and share both X row panels and W column panels in L2.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int tiles = tiles_m * tiles_n;
+    const int q = tiles >> 3;
+    int t = wg;
+    if (wg < (q << 3)) t = (wg & 7) * q + (wg >> 3);
+    const int per_group = GROUP_M * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * GROUP_M;
+    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int r = t - g * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+gemm_epi_kernel(GemmArgs a)
+{
+    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int LDK = BK + 4;             // padded LDS row stride, floats
+    constexpr int STAGE = (BM + BN) * LDK;  // floats per LDS stage
+    constexpr int TM = BM / WAVES_M;        // wave tile
+    constexpr int TN = BN / WAVES_N;
+    constexpr int FM = TM / 32;             // 32x32 MFMA blocks per wave
+    constexpr int FN = TN / 32;
+    constexpr int C4 = BK / 4;              // float4 per tile row
+    constexpr int A_LD = BM * C4 / NT;      // float4 global loads per thread
+    constexpr int B_LD = BN * C4 / NT;
+    static_assert(BK % 8 == 0 && TM % 32 == 0 && TN % 32 == 0, "tile shape");
+    static_assert((BM * C4) % NT == 0 && (BN * C4) % NT == 0, "load split");
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WAVES_N;
+    const int wn = wave % WAVES_N;
+
+    int tm, tn;
+    tile_of<8>(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int M = a.M, N = a.N, K = a.K;
+
+    const int kbeg = blockIdx.y * a.k_slice;
+    const int kend = min(K, kbeg + a.k_slice);
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+    f32x4 ra[A_LD], rb[B_LD];
+
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            const int idx = tid + i * NT;
+            const int row = idx / C4;
+            const int gk = k0 + (idx % C4) * 4;
+            const int gm = m0 + row;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (gm < M && gk < kend) v = *reinterpret_cast<const f32x4 *>(a.X + (int64_t)gm * K + gk);
+            ra[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) {
+            const int idx = tid + i * NT;
+            const int row = idx / C4;
+            const int gk = k0 + (idx % C4) * 4;
+            const int gn = n0 + row;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (gn < N && gk < kend) v = *reinterpret_cast<const f32x4 *>(a.W + (int64_t)gn * K + gk);
+            rb[i] = v;
+        }
+    };
+    auto sstore = [&](int buf) {
+        float *As = smem + buf * STAGE;
+        float *Bs = As + BM * LDK;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            const int idx = tid + i * NT;
+            *reinterpret_cast<f32x4 *>(As + (idx / C4) * LDK + (idx % C4) * 4) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) {
+            const int idx = tid + i * NT;
+            *reinterpret_cast<f32x4 *>(Bs + (idx / C4) * LDK + (idx % C4) * 4) = rb[i];
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 4;
+
+    if (nk > 0) {
+        gload(kbeg);
+        sstore(0);
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 1 < nk;
+        if (more) gload(kbeg + (kt + 1) * BK);
+        const float *As = smem + (kt & 1) * STAGE;
+        const float *Bs = As + BM * LDK;
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 8) {
+            f32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const f32x4 *>(As + (wm * TM + i * 32 + frag_row) * LDK + kk + frag_k);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const f32x4 *>(Bs + (wn * TN + j * 32 + frag_row) * LDK + kk + frag_k);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][c], bf[j][c], acc[i][j], 0, 0, 0);
+        }
+        if (more) sstore((kt + 1) & 1);
+        __syncthreads();
+    }
+
+    // ------------------------------------------------------------------ epilogue
+    const int col_in_block = lane & 31;
+    const int row_half = (lane >> 5) * 4;
+
+    if constexpr (EPI == EPI_SPLITK_PARTIAL) {
+        float *P = a.out + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * TN + j * 32 + col_in_block;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + row_half + (r & 3);
+                    if (m < M && n < N) P[(int64_t)m * N + n] = acc[i][j][r];
+                }
+        }
+    } else if constexpr (EPI == EPI_POOL_GELU_SCALE_ROWMAX) {
+        // AvgPool1d(16): a 16-wide window is 16 consecutive columns, i.e. the
+        // 16 lanes of one quarter-wavefront holding the same row; sum them
+        // with butterfly shuffles.  Window j is kept only if it lies wholly
+        // inside N (floor mode).  Then GELU, scale, and the max over this
+        // workgroup's windows of each row; the max over column tiles is done
+        // by a second, deterministic pass.
+        const int L = N >> 4;
+        float rowmax[FM][16];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rowmax[i][r] = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * TN + j * 32 + col_in_block;
+            const float bn = n < N ? a.bias[n] : 0.f;
+            const int win = (n0 + wn * TN + j * 32 + (col_in_block & 16)) >> 4;
+            const bool win_ok = win < L;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = acc[i][j][r] + bn;
+                    v += __shfl_xor(v, 1);
+                    v += __shfl_xor(v, 2);
+                    v += __shfl_xor(v, 4);
+                    v += __shfl_xor(v, 8);
+                    const float g = gelu_erf(v * 0.0625f) * a.tail.scale;
+                    rowmax[i][r] = fmaxf(rowmax[i][r], win_ok ? g : -INFINITY);
+                }
+        }
+        __syncthreads();  // LDS stages are free now; reuse them for the cross-wave max
+        float *red = smem;  // [WAVES_N][BM]
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = rowmax[i][r];
+                v = fmaxf(v, __shfl_xor(v, 16));
+                if ((lane & 31) == 0) red[wn * BM + wm * TM + i * 32 + (r >> 2) * 8 + row_half + (r & 3)] = v;
+            }
+        __syncthreads();
+        for (int t = tid; t < BM; t += NT) {
+            const int m = m0 + t;
+            if (m < M) {
+                float v = red[t];
+#pragma unroll
+                for (int w = 1; w < WAVES_N; ++w) v = fmaxf(v, red[w * BM + t]);
+                a.out[(int64_t)m * a.tiles_n + tn] = v;
+            }
+        }
+    } else {
+        using Tail = typename std::conditional<
+            EPI == EPI_SCALE_HARDTANH_GELU, TailScaleHardtanhGelu,
+            typename std::conditional<EPI == EPI_SWISH_SCALE, TailSwishScale, TailNone>::type>::type;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * TN + j * 32 + col_in_block;
+            const bool n_ok = n < N;
+            const float bn = n_ok ? a.bias[n] : 0.f;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + row_half + (r & 3);
+                    if (m < M && n_ok) a.out[(int64_t)m * N + n] = Tail::apply(acc[i][j][r] + bn, a.tail);
+                }
+        }
+    }
+}
+
+// Second pass of split-K: Y[m,n] = tail(sum_{s=0..S-1} P[s,m,n] + b[n]), the
+// slices added in increasing s, so the result is the same on every run.
+template <int EPI>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *P, const float *bias, float *Y,
+                                                            int64_t MN, int32_t N, int32_t S, TailParams tail)
+{
+    using Tail = typename std::conditional<
+        EPI == EPI_SCALE_HARDTANH_GELU, TailScaleHardtanhGelu,
+        typename std::conditional<EPI == EPI_SWISH_SCALE, TailSwishScale, TailNone>::type>::type;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += stride) {
+        float s = P[e];
+        for (int k = 1; k < S; ++k) s += P[(int64_t)k * MN + e];
+        Y[e] = Tail::apply(s + bias[e % N], tail);
+    }
+}
+
+// Second pass of tail (b): Y[m] = max over column tiles of the per-tile row
+// maxima.  Max is exact, so the result does not depend on order.
+__global__ void __launch_bounds__(256) rowmax_finalize_kernel(const float *part, float *Y, int32_t M,
+                                                              int32_t tiles_n)
+{
+    const int m = blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= M) return;
+    const float *p = part + (int64_t)m * tiles_n;
+    float v = p[0];
+    for (int t = 1; t < tiles_n; ++t) v = fmaxf(v, p[t]);
+    Y[m] = v;
+}
+
+}  // namespace lin_epi

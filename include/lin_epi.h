@@ -1,0 +1,137 @@
+/*
+ * lin_epi -- fp32 linear layer Y = X * W^T + b with its elementwise tail fused
+ * into the GEMM epilogue, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is nn.Linear followed by one of three tails, as the pages
+ * state the problems:
+ *
+ *   kind 1, scale -> Hardtanh(min, max) -> exact-erf GELU
+ *       page "Kimi-K2.6 l2_p53" (POPCORNBENCH), problem statement: GEMM,
+ *       scale by a constant, Hardtanh clamp, GELU.
+ *   kind 2, AvgPool1d(16, stride 16, no padding, floor mode) over the output
+ *       features -> exact-erf GELU -> scale -> max over the pooled features
+ *       page "Kimi-K2.6 l2_p98", its step-by-step reading of the reference
+ *       model (Linear, AvgPool1d defaults, GELU, scale, max over dim 1).
+ *   kind 3, swish y * sigmoid(y) -> scale
+ *       page "Kimi-K2.6 l2_p59", problem analysis (swish, then scaling).
+ *   kind 0, no tail (the plain linear layer), for tests.
+ *
+ * GELU is 0.5 * x * (1 + erf(x / sqrt 2)) (PyTorch's default form, which
+ * page l2_p53 settles on).  All arithmetic is IEEE binary32: fp32 products
+ * and fp32 accumulation on the matrix cores; no reduced-precision path.
+ *
+ * Memory: every pointer argument of lin_epi_run is a DEVICE pointer on the
+ * current HIP device, owned by the caller, row-major and densely packed:
+ *   X [M, K], W [N, K] (each output feature's weights K-contiguous, the
+ *   nn.Linear weight layout), b [N], Y [M, N] for kinds 0, 1, 3 and Y [M]
+ *   for kind 2.
+ * X and W must be 16-byte aligned and K a multiple of 4 (rows are read with
+ * 128-bit loads); Y must be 4-byte aligned.  Y must not alias X, W or b.
+ *
+ * Threading and streams: a handle is bound to one HIP stream at creation and
+ * is not thread-safe.  lin_epi_run only enqueues work on that stream and
+ * returns; the caller synchronises.  The handle owns a device workspace
+ * (split-K partial sums, per-tile row maxima) that grows on demand; two runs
+ * in flight on the same handle share it, which is safe because they are
+ * ordered on the handle's stream.
+ *
+ * Errors: every call returns a status code (LIN_EPI_OK = 0 or a negative
+ * LIN_EPI_E* value).  Arguments are validated on the host before any HIP
+ * call, so an invalid call enqueues nothing and leaves Y untouched.
+ */
+#ifndef LIN_EPI_H
+#define LIN_EPI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lin_epi_ctx *lin_epi_handle;
+
+typedef enum {
+    LIN_EPI_NONE = 0,                   /* Y = X W^T + b */
+    LIN_EPI_SCALE_HARDTANH_GELU = 1,    /* Y = GELU(clamp((XW^T+b)*scale, ht_min, ht_max)) */
+    LIN_EPI_POOL_GELU_SCALE_ROWMAX = 2, /* Y[m] = max_j scale*GELU(mean_{t<16} y[m,16j+t]) */
+    LIN_EPI_SWISH_SCALE = 3             /* Y = (y * sigmoid(y)) * scale */
+} lin_epi_kind;
+
+/* Tail parameters.  Fields a kind does not use are ignored. */
+typedef struct {
+    int32_t kind;        /* lin_epi_kind */
+    float scale;         /* kinds 1, 2, 3 */
+    float ht_min;        /* kind 1: Hardtanh lower bound (inclusive clamp) */
+    float ht_max;        /* kind 1: Hardtanh upper bound, ht_min <= ht_max */
+    int32_t pool_kernel; /* kind 2: must be 16 */
+    int32_t pool_stride; /* kind 2: must equal pool_kernel (AvgPool1d default) */
+} lin_epi_desc;
+
+enum {
+    LIN_EPI_OK = 0,
+    LIN_EPI_EINVAL = -1,  /* null handle/pointer/desc, negative size, unknown kind, ht_min > ht_max */
+    LIN_EPI_EALIGN = -2,  /* X or W not 16-byte aligned, K % 4 != 0, Y not 4-byte aligned */
+    LIN_EPI_ENOTSUP = -3, /* kind 2 with pool_kernel != 16, pool_stride != pool_kernel, or N < 16 */
+    LIN_EPI_ENOMEM = -4,  /* workspace allocation failed */
+    LIN_EPI_EHIP = -5     /* a HIP call or kernel launch failed */
+};
+
+/* Create a handle bound to `hip_stream` (a hipStream_t; NULL = the default
+ * stream).  Makes no device allocation.  *out is set to NULL on failure. */
+int lin_epi_create(lin_epi_handle *out, void *hip_stream);
+
+/* Enqueue Y = tail(X W^T + b) on the handle's stream.
+ * M == 0 or N == 0 is a successful no-op.  K == 0 is allowed and gives
+ * Y = tail(b) broadcast over the rows (the empty sum is 0); X and W may then
+ * be NULL.  b must not be NULL (every layer on the pages has a bias). */
+int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K,
+                const float *X, const float *W, const float *b,
+                const lin_epi_desc *desc, float *Y);
+
+/* Release the handle and its workspace (waits for the handle's stream
+ * first).  NULL is a no-op. */
+int lin_epi_destroy(lin_epi_handle h);
+
+/* Static string for a status code. */
+const char *lin_epi_status_string(int status);
+
+/* ---- tuning and introspection (not needed for ordinary use) ------------- */
+
+enum {
+    /* Split-K control: 0 = automatic (default), 1 = never split, S >= 2 =
+     * split K into S slices whose partial sums are added in slice order by
+     * a second pass (deterministic).  Split-K applies to kinds 0, 1 and 3. */
+    LIN_EPI_OPT_SPLIT_K = 1,
+    /* 1 = time every kernel this handle launches with HIP events on its
+     * stream (read with lin_epi_profile_read); 0 = off (default). */
+    LIN_EPI_OPT_PROFILE = 2
+};
+
+int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value);
+
+/* What the last successful lin_epi_run launched. */
+typedef struct {
+    int32_t tile_m, tile_n, tile_k; /* workgroup output tile and K step */
+    int32_t split_k;                /* K slices (1 = no split) */
+    int64_t grid_main;              /* workgroups of the GEMM kernel */
+    int32_t kernels;                /* kernels launched (GEMM + reduce/finalize) */
+    int64_t workspace_bytes;        /* workspace the run used */
+} lin_epi_plan;
+
+int lin_epi_last_plan(lin_epi_handle h, lin_epi_plan *out);
+
+/* Accumulated kernel timings since the last read (profiling on).  Waits for
+ * the handle's stream.  Role 0 is the GEMM kernel, role 1 the second pass
+ * (split-K reduce or row-max finalize). */
+typedef struct {
+    int64_t launches[2];
+    double total_ms[2];
+} lin_epi_profile;
+
+int lin_epi_profile_read(lin_epi_handle h, lin_epi_profile *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIN_EPI_H */

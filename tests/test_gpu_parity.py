@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, to |gpu - ref| <= 1e-3 * (1 + |ref|) on every checked
+element, bit-exact where the exact result is representable."""
+
+import numpy as np
+import pytest
+
+import dense_linear_layer_amd as lib
+import oracle
+import workloads
+from parity_util import compare, desc_for, log, oracle_rows, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def h():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with lib.LinEpi() as handle:
+        yield handle
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    log("== %s" % request.node.nodeid)
+
+
+ALL_TAILS = (workloads.TAIL_A, workloads.TAIL_B, workloads.TAIL_C, workloads.TAIL_NONE)
+
+
+# ---------------------------------------------------------------- small shapes
+
+def test_tiny_config_tail_a(h):
+    w = workloads.WORKLOADS["tiny"]
+    X, W, b = workloads.make_inputs(w.M, w.N, w.K, seed=w.seed)
+    got = run_gpu(h, *to_dev(X, W, b), workloads.TAIL_A)
+    compare(got, oracle_rows(X, W, b, workloads.TAIL_A), what="tiny tail a")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (37, 200, 68), (129, 130, 36), (1, 1, 4), (7, 33, 4),
+                                   (300, 17, 1028), (1000, 6000, 4100)])
+def test_integer_inputs_bit_exact(h, M, N, K):
+    """Integer-valued inputs: every partial sum is an exact fp32 integer, so the
+    GPU must reproduce the oracle bit for bit whatever its summation order.
+    Pins indexing, K tail and edge masking."""
+    X, W, b = workloads.integer_inputs(M, N, K, seed=M + N + K)
+    got = run_gpu(h, *to_dev(X, W, b), workloads.TAIL_NONE)
+    ref = oracle.linear_rows(X, W, b)
+    assert np.array_equal(got.astype(np.float64), ref), "max|d| = %g" % np.abs(got - ref).max()
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 48, 12), (130, 290, 100), (257, 64, 520), (64, 16, 8), (33, 1000, 4)])
+@pytest.mark.parametrize("tail", ALL_TAILS, ids=lambda t: t.name)
+def test_odd_shapes_all_tails(h, M, N, K, tail):
+    X, W, b = workloads.make_inputs(M, N, K, seed=3 * M + N)
+    got = run_gpu(h, *to_dev(X, W, b), tail)
+    compare(got, oracle_rows(X, W, b, tail), what="%dx%dx%d %s" % (M, N, K, tail.name))
+
+
+def test_ragged_config_all_tails_on_one_gemm(h):
+    """1000x6000x4100: not tile multiples; the three tails run on the same X, W, b
+    (tail (b) pools 6000 columns into 375 windows)."""
+    w = workloads.WORKLOADS["ragged_1000x6000x4100"]
+    X, W, b = workloads.make_inputs(w.M, w.N, w.K, seed=w.seed)
+    Xd, Wd, bd = to_dev(X, W, b)
+    y = oracle.linear_rows(X, W, b)
+    for tail in w.tails:
+        got = run_gpu(h, Xd, Wd, bd, tail)
+        ref = oracle.apply_tail(y, tail.kind, **tail.params())
+        compare(got, ref, what="ragged %s" % tail.name)
+        if tail.kind == workloads.POOL_GELU_SCALE_ROWMAX:
+            _, g, _ = oracle.tail_pool_gelu_scale_rowmax(y, 16, tail.scale)
+            assert g.shape[1] == 375
+
+
+def test_k_zero_gives_tail_of_bias(h):
+    M, N = 70, 300
+    b = workloads.make_inputs(1, N, 4, seed=11)[2]
+    X = torch.empty((M, 0), dtype=torch.float32, device="cuda:0")
+    W = torch.empty((N, 0), dtype=torch.float32, device="cuda:0")
+    bd = to_dev(b)[0]
+    for tail in ALL_TAILS:
+        got = run_gpu(h, X, W, bd, tail)
+        ref = oracle.apply_tail(np.tile(b.astype(np.float64), (M, 1)), tail.kind, **tail.params())
+        compare(got, ref, what="K=0 %s" % tail.name)
+
+
+# ------------------------------------------------- epilogue functors, tightly
+
+def _functor_inputs(n_values: int):
+    """X = I_K and b = 0 make the GEMM exact: Y[m, n] = W[n, m].  W carries a
+    dense grid of values in [-10, 10] plus the clamp points and their
+    neighbours, so Y = tail(W^T) exposes the epilogue math alone."""
+    vals = np.linspace(-10, 10, n_values - 12).astype(np.float32)
+    extra = np.array([0.0, -0.0, 2.0, -2.0, 4.0, -4.0, np.nextafter(np.float32(4), np.float32(5)),
+                      np.nextafter(np.float32(4), np.float32(3)), np.nextafter(np.float32(-4), np.float32(-5)),
+                      np.nextafter(np.float32(-4), np.float32(-3)), 1.0, -1.0], dtype=np.float32)
+    vals = np.concatenate([vals, extra])
+    K = 128
+    N = vals.size // K
+    W = vals[: N * K].reshape(N, K).copy()
+    X = np.eye(K, dtype=np.float32)
+    b = np.zeros(N, dtype=np.float32)
+    return X, W, b
+
+
+@pytest.mark.parametrize("tail", [workloads.TAIL_A, workloads.TAIL_C, workloads.TAIL_NONE], ids=lambda t: t.name)
+def test_epilogue_functor_accuracy(h, tail):
+    X, W, b = _functor_inputs(128 * 96)
+    got = run_gpu(h, *to_dev(X, W, b), tail)
+    ref = oracle_rows(X, W, b, tail)
+    err = np.abs(got.astype(np.float64) - ref)
+    rel = (err / (1.0 + np.abs(ref))).max()
+    log("functor %s max|d| = %.3g, max|d|/(1+|ref|) = %.3g" % (tail.name, err.max(), rel))
+    # a few fp32 ulp of the output; erf-GELU and tanh-GELU differ by up to 4.7e-4
+    assert rel <= 2e-6
+
+
+def test_tail_a_clipping_exercised(h):
+    """X scaled by 10 so that about half of y*0.5 lies outside [-2, 2]."""
+    X, W, b = workloads.make_inputs(300, 520, 256, seed=21)
+    X *= np.float32(10.0)
+    y = oracle.linear_rows(X, W, b)
+    frac = float((np.abs(0.5 * y) > 2).mean())
+    assert frac > 0.3
+    got = run_gpu(h, *to_dev(X, W, b), workloads.TAIL_A)
+    compare(got, oracle.apply_tail(y, workloads.SCALE_HARDTANH_GELU, **workloads.TAIL_A.params()),
+            what="clipping tail a (%.0f%% clipped)" % (100 * frac))
+
+
+# ------------------------------------------------------------------ split-K
+
+@pytest.mark.parametrize("S", [2, 3, 5])
+@pytest.mark.parametrize("tail", [workloads.TAIL_A, workloads.TAIL_C, workloads.TAIL_NONE], ids=lambda t: t.name)
+def test_forced_split_k(tail, S):
+    M, N, K = 200, 390, 1000
+    X, W, b = workloads.make_inputs(M, N, K, seed=31)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, S)
+        Xd, Wd, bd = to_dev(X, W, b)
+        got = run_gpu(h, Xd, Wd, bd, tail)
+        assert h.plan().split_k == S and h.plan().kernels == 2
+        compare(got, oracle_rows(X, W, b, tail), what="split-K %d %s" % (S, tail.name))
+        again = [run_gpu(h, Xd, Wd, bd, tail) for _ in range(2)]
+        for a in again:
+            assert np.array_equal(a, got), "split-K rerun not bitwise identical"
+
+
+def test_split_k_integer_exact():
+    X, W, b = workloads.integer_inputs(130, 260, 2052, seed=32)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, 4)
+        got = run_gpu(h, *to_dev(X, W, b), workloads.TAIL_NONE)
+        assert h.plan().split_k == 4
+    assert np.array_equal(got.astype(np.float64), oracle.linear_rows(X, W, b))
+
+
+# ------------------------------------------------------------- determinism
+
+def test_rowmax_deterministic(h):
+    X, W, b = workloads.make_inputs(500, 3000, 520, seed=41)
+    Xd, Wd, bd = to_dev(X, W, b)
+    outs = [run_gpu(h, Xd, Wd, bd, workloads.TAIL_B) for _ in range(3)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    compare(outs[0], oracle_rows(X, W, b, workloads.TAIL_B), what="rowmax 500x3000x520")
+
+
+# ---------------------------------------------------------------- guard bands
+
+@pytest.mark.parametrize("tail", ALL_TAILS, ids=lambda t: t.name)
+def test_output_guard_bands_untouched(h, tail):
+    M, N, K = 131, 200, 36
+    X, W, b = workloads.make_inputs(M, N, K, seed=51)
+    Xd, Wd, bd = to_dev(X, W, b)
+    n_out = M if tail.kind == workloads.POOL_GELU_SCALE_ROWMAX else M * N
+    pad = 4096
+    buf = torch.full((n_out + 2 * pad,), float("nan"), dtype=torch.float32, device="cuda:0")
+    Y = buf[pad: pad + n_out]
+    h.run_into(Xd, Wd, bd, desc_for(tail), Y)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.isnan(host[:pad]).all() and np.isnan(host[pad + n_out:]).all(), "write outside Y"
+    ref = oracle_rows(X, W, b, tail)
+    compare(host[pad: pad + n_out].reshape(ref.shape), ref, what="guarded %s" % tail.name)
+
+
+def test_non_default_stream():
+    X, W, b = workloads.make_inputs(260, 300, 64, seed=61)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi(stream=s) as h:
+        with torch.cuda.stream(s):
+            Y = h.run(Xd, Wd, bd, desc_for(workloads.TAIL_C))
+        s.synchronize()
+        compare(Y.cpu().numpy(), oracle_rows(X, W, b, workloads.TAIL_C), what="side stream")
+
+
+# ------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", ["p1_2048x8192x8192", "p2_1024x8192x8192", "p3_128x32768x32768"])
+def test_full_size_workload_checked_rows(h, name):
+    """The large shapes at full size, in the launch configuration the benchmark
+    times, checked on 64 seeded rows (all N outputs of each row)."""
+    w = workloads.WORKLOADS[name]
+    log("generating %s" % name)
+    X, W, b = workloads.make_inputs(w.M, w.N, w.K, seed=w.seed)
+    Xd, Wd, bd = to_dev(X, W, b)
+    rows = workloads.checked_rows(w.M, seed=w.seed)
+    tail = w.tails[0]
+    log("running %s on the GPU (plan follows)" % name)
+    got = run_gpu(h, Xd, Wd, bd, tail)
+    p = h.plan()
+    log("plan: tile %dx%dx%d split %d grid %d kernels %d" % (p.tile_m, p.tile_n, p.tile_k, p.split_k, p.grid_main,
+                                                            p.kernels))
+    del Wd
+    torch.cuda.empty_cache()
+    log("oracle on %d rows" % rows.size)
+    ref = oracle_rows(X, W, b, tail, rows)
+    compare(got[rows], ref, what="%s %s (64 rows)" % (name, tail.name))
