@@ -92,7 +92,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="p1_2048x8192x8192", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--tail", type=int, default=None, help="tail index within the workload (default 0)")
     ap.add_argument("--split-k", type=int, default=0, help="0 auto, 1 off, S>=2 forced")
