@@ -81,11 +81,21 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int &t
     tn = r / gm;
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+// A workgroup tile shape: BM x BN outputs, K step BK, WAVES_M x WAVES_N
+// wavefronts each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    static constexpr int LDS_BYTES = 2 * (BM + BN) * (BK + 4) * 4;
+};
+
+template <class Cfg, int EPI>
+__global__ void __launch_bounds__(Cfg::THREADS)
 gemm_epi_kernel(GemmArgs a)
 {
-    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WAVES_M = Cfg::WAVES_M, WAVES_N = Cfg::WAVES_N;
+    constexpr int NT = Cfg::THREADS;
     constexpr int LDK = BK + 4;             // padded LDS row stride, floats
     constexpr int STAGE = (BM + BN) * LDK;  // floats per LDS stage
     constexpr int TM = BM / WAVES_M;        // wave tile
@@ -222,29 +232,13 @@ gemm_epi_kernel(GemmArgs a)
         // workgroup's windows of each row; the max over column tiles is done
         // by a second, deterministic pass.
         const int L = N >> 4;
-        float rowmax[FM][16];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) rowmax[i][r] = -INFINITY;
+        float bn[FN];
+        bool win_ok[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int n = n0 + wn * TN + j * 32 + col_in_block;
-            const float bn = n < N ? a.bias[n] : 0.f;
-            const int win = (n0 + wn * TN + j * 32 + (col_in_block & 16)) >> 4;
-            const bool win_ok = win < L;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float v = acc[i][j][r] + bn;
-                    v += __shfl_xor(v, 1);
-                    v += __shfl_xor(v, 2);
-                    v += __shfl_xor(v, 4);
-                    v += __shfl_xor(v, 8);
-                    const float g = gelu_erf(v * 0.0625f) * a.tail.scale;
-                    rowmax[i][r] = fmaxf(rowmax[i][r], win_ok ? g : -INFINITY);
-                }
+            bn[j] = n < N ? a.bias[n] : 0.f;
+            win_ok[j] = ((n0 + wn * TN + j * 32 + (col_in_block & 16)) >> 4) < L;
         }
         __syncthreads();  // LDS stages are free now; reuse them for the cross-wave max
         float *red = smem;  // [WAVES_N][BM]
@@ -252,9 +246,19 @@ gemm_epi_kernel(GemmArgs a)
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float v = rowmax[i][r];
-                v = fmaxf(v, __shfl_xor(v, 16));
-                if ((lane & 31) == 0) red[wn * BM + wm * TM + i * 32 + (r >> 2) * 8 + row_half + (r & 3)] = v;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    float v = acc[i][j][r] + bn[j];
+                    v += __shfl_xor(v, 1);
+                    v += __shfl_xor(v, 2);
+                    v += __shfl_xor(v, 4);
+                    v += __shfl_xor(v, 8);
+                    const float g = gelu_erf(v * 0.0625f) * a.tail.scale;
+                    mx = fmaxf(mx, win_ok[j] ? g : -INFINITY);
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                if ((lane & 31) == 0) red[wn * BM + wm * TM + i * 32 + (r >> 2) * 8 + row_half + (r & 3)] = mx;
             }
         __syncthreads();
         for (int t = tid; t < BM; t += NT) {

@@ -13,10 +13,31 @@ using namespace lin_epi;
 
 namespace {
 
-// One tile configuration: 128x128 output tile, K step 32, four wavefronts
-// in a 2x2 arrangement (64x64 per wavefront = 2x2 MFMA 32x32 blocks).
-constexpr int BM = 128, BN = 128, BK = 32, WAVES_M = 2, WAVES_N = 2;
-constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+// Tile table.  All three use v_mfma_f32_32x32x2_f32, a K step of 32 and a
+// double-buffered LDS stage; they differ in workgroup tile and wavefront
+// count, and the dispatcher picks one per call (choose_plan below):
+//   LARGE  256x256, 8 wavefronts (4x2, 64x128 each), 144 KiB LDS, 1 WG/CU
+//   MID    128x256, 8 wavefronts (2x4, 64x64 each),  108 KiB LDS, 1 WG/CU
+//   SMALL  128x128, 4 wavefronts (2x2, 64x64 each),   72 KiB LDS, 2 WG/CU
+using CfgLarge = TileCfg<256, 256, 32, 4, 2>;
+using CfgMid = TileCfg<128, 256, 32, 2, 4>;
+using CfgSmall = TileCfg<128, 128, 32, 2, 2>;
+
+enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_COUNT = 3 };
+
+struct CfgInfo {
+    int bm, bn, bk, wgs_per_cu;
+    double speed;  // relative MFMA efficiency at full occupancy (measured on MI355X)
+};
+
+constexpr CfgInfo kCfgs[CFG_COUNT] = {
+    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, 1, 1.035},
+    {CfgMid::BM, CfgMid::BN, CfgMid::BK, 1, 1.01},
+    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, 2, 1.0},
+};
+static_assert(CfgLarge::LDS_BYTES <= 160 * 1024 && CfgMid::LDS_BYTES <= 160 * 1024 &&
+                  2 * CfgSmall::LDS_BYTES <= 160 * 1024,
+              "LDS budget");
 
 struct PendingTiming {
     int role;
@@ -90,11 +111,21 @@ int timed_launch(lin_epi_ctx *h, int role, Launch &&launch)
     return LIN_EPI_OK;
 }
 
-template <int EPI>
-void launch_gemm(const GemmArgs &g, int64_t grid_x, int split, hipStream_t s)
+template <class Cfg, int EPI>
+void launch_gemm_cfg(const GemmArgs &g, int64_t grid_x, int split, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_epi_kernel<BM, BN, BK, WAVES_M, WAVES_N, EPI>), dim3((unsigned)grid_x, (unsigned)split),
-                       dim3(THREADS), 0, s, g);
+    hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI>), dim3((unsigned)grid_x, (unsigned)split), dim3(Cfg::THREADS), 0, s,
+                       g);
+}
+
+template <int EPI>
+void launch_gemm(int cfg, const GemmArgs &g, int64_t grid_x, int split, hipStream_t s)
+{
+    switch (cfg) {
+        case CFG_LARGE: launch_gemm_cfg<CfgLarge, EPI>(g, grid_x, split, s); break;
+        case CFG_MID: launch_gemm_cfg<CfgMid, EPI>(g, grid_x, split, s); break;
+        default: launch_gemm_cfg<CfgSmall, EPI>(g, grid_x, split, s); break;
+    }
 }
 
 template <int EPI>
@@ -106,19 +137,62 @@ void launch_reduce(const float *P, const float *bias, float *Y, int64_t MN, int 
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, s, P, bias, Y, MN, N, S, t);
 }
 
-// Split-K slices for the elementwise tails: only when the output tiles alone
-// cannot give every compute unit two workgroups and K is long enough that
-// each slice still runs many K steps.
-int choose_split(const lin_epi_ctx *h, int64_t tiles, int64_t K, int kind)
+struct Plan {
+    int cfg;
+    int split;
+    int64_t k_slice;
+    int tiles_m, tiles_n;
+};
+
+// Pick the tile configuration and the number of K slices.  For every
+// candidate the model scores
+//   speed(cfg) * useful(cfg) * balance(cfg, S) / (1 + reduce_cost(S)),
+// where useful is the fraction of computed outputs that lie inside M x N,
+// balance is the fraction of workgroup slots busy over the rounds needed to
+// run tiles*S workgroups on this device, and reduce_cost is the second pass
+// relative to the GEMM: S partial reads plus one output write of M*N floats
+// at ~4 TB/s against 2*M*N*K FLOP at ~120 TFLOP/s, i.e. (S + 1) * 60 / K.
+// A slice keeps at least 8 K steps.  Tail (b) never splits (its pooling and
+// row max act on complete sums).  LIN_EPI_OPT_SPLIT_K overrides S.
+Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind)
 {
-    if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX) return 1;
-    if (h->split_opt == 1) return 1;
-    if (h->split_opt >= 2) return (int)h->split_opt;
-    const int64_t slots = 2 * (int64_t)h->num_cus;
-    if (tiles * 2 > slots || K < 8192) return 1;
-    int64_t s = slots / tiles;
-    if (s > 4) s = 4;
-    return (int)(s < 2 ? 1 : s);
+    Plan best{CFG_SMALL, 1, 0, 0, 0};
+    double best_score = -1.0;
+    for (int c = 0; c < CFG_COUNT; ++c) {
+        const CfgInfo &ci = kCfgs[c];
+        const int64_t tm = (M + ci.bm - 1) / ci.bm, tn = (N + ci.bn - 1) / ci.bn;
+        const int64_t tiles = tm * tn;
+        const double useful = (double)M * (double)N / ((double)tm * ci.bm * (double)tn * ci.bn);
+        const int64_t slots = (int64_t)h->num_cus * ci.wgs_per_cu;
+        const int64_t steps = (K + ci.bk - 1) / ci.bk;
+        int s_lo = 1, s_hi = 8;
+        if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX || h->split_opt == 1) s_hi = 1;
+        if (h->split_opt >= 2) s_lo = s_hi = (int)h->split_opt;
+        for (int S = s_lo; S <= s_hi; ++S) {
+            if (S > 1 && h->split_opt < 2 && steps < 8 * S) break;
+            if (S > 1 && S > steps) break;
+            const int64_t units = tiles * S;
+            const int64_t rounds = (units + slots - 1) / slots;
+            const double balance = (double)units / (double)(rounds * slots);
+            const double reduce_cost = S > 1 ? (S + 1) * 60.0 / (double)K : 0.0;
+            const double score = ci.speed * useful * balance / (1.0 + reduce_cost);
+            if (score > best_score) {
+                best_score = score;
+                best = Plan{c, S, 0, (int)tm, (int)tn};
+            }
+        }
+    }
+    const CfgInfo &ci = kCfgs[best.cfg];
+    const int64_t steps = (K + ci.bk - 1) / ci.bk;
+    if (best.split > 1 && steps > 0) {
+        best.k_slice = (steps + best.split - 1) / best.split * ci.bk;
+        best.split = (int)((K + best.k_slice - 1) / best.k_slice);
+    }
+    if (best.split <= 1) {
+        best.split = 1;
+        best.k_slice = steps > 0 ? steps * ci.bk : ci.bk;
+    }
+    return best;
 }
 
 }  // namespace
@@ -237,24 +311,11 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
     int rc = ensure_device(h);
     if (rc != LIN_EPI_OK) return rc;
 
-    const int tiles_m = (int)((M + BM - 1) / BM);
-    const int tiles_n = (int)((N + BN - 1) / BN);
+    const Plan pl = choose_plan(h, M, N, K, kind);
+    const int tiles_m = pl.tiles_m, tiles_n = pl.tiles_n;
     const int64_t tiles = (int64_t)tiles_m * tiles_n;
-    int split = choose_split(h, tiles, K, kind);
-    // every slice must own at least one K step
-    int64_t k_slice = K;
-    if (split > 1) {
-        const int64_t steps = (K + BK - 1) / BK;
-        if (split > steps) split = (int)(steps > 0 ? steps : 1);
-        k_slice = ((steps + split - 1) / split) * BK;
-        split = (int)((K + k_slice - 1) / k_slice);
-        if (split < 1) split = 1;
-    }
-    if (split <= 1) {
-        split = 1;
-        k_slice = (K + BK - 1) / BK * BK;
-        if (k_slice == 0) k_slice = BK;
-    }
+    const int split = pl.split;
+    const int64_t k_slice = pl.k_slice;
 
     GemmArgs g{};
     g.X = X;
@@ -269,9 +330,9 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
     g.tail = TailParams{desc->scale, desc->ht_min, desc->ht_max};
 
     lin_epi_plan plan{};
-    plan.tile_m = BM;
-    plan.tile_n = BN;
-    plan.tile_k = BK;
+    plan.tile_m = kCfgs[pl.cfg].bm;
+    plan.tile_n = kCfgs[pl.cfg].bn;
+    plan.tile_k = kCfgs[pl.cfg].bk;
     plan.split_k = split;
     plan.grid_main = tiles * split;
 
@@ -281,7 +342,7 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         rc = ensure_workspace(h, bytes);
         if (rc != LIN_EPI_OK) return rc;
         g.out = static_cast<float *>(h->ws);
-        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(g, tiles, 1, s); });
+        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s); });
         if (rc != LIN_EPI_OK) return rc;
         const float *part = static_cast<const float *>(h->ws);
         const int32_t Mi = (int32_t)M;
@@ -297,7 +358,7 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         rc = ensure_workspace(h, bytes);
         if (rc != LIN_EPI_OK) return rc;
         g.out = static_cast<float *>(h->ws);
-        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(g, tiles, split, s); });
+        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s); });
         if (rc != LIN_EPI_OK) return rc;
         const float *P = static_cast<const float *>(h->ws);
         const int64_t MN = M * N;
@@ -317,9 +378,9 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         g.out = Y;
         rc = timed_launch(h, 0, [&] {
             switch (kind) {
-                case LIN_EPI_NONE: launch_gemm<EPI_NONE>(g, tiles, 1, s); break;
-                case LIN_EPI_SCALE_HARDTANH_GELU: launch_gemm<EPI_SCALE_HARDTANH_GELU>(g, tiles, 1, s); break;
-                default: launch_gemm<EPI_SWISH_SCALE>(g, tiles, 1, s); break;
+                case LIN_EPI_NONE: launch_gemm<EPI_NONE>(pl.cfg, g, tiles, 1, s); break;
+                case LIN_EPI_SCALE_HARDTANH_GELU: launch_gemm<EPI_SCALE_HARDTANH_GELU>(pl.cfg, g, tiles, 1, s); break;
+                default: launch_gemm<EPI_SWISH_SCALE>(pl.cfg, g, tiles, 1, s); break;
             }
         });
         if (rc != LIN_EPI_OK) return rc;
