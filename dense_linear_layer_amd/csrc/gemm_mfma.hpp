@@ -82,16 +82,19 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int &t
 }
 
 // A workgroup tile shape: BM x BN outputs, K step BK, WAVES_M x WAVES_N
-// wavefronts each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile.
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+// wavefronts each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile, and the
+// number of workgroups meant to share one compute unit (register budget).
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WG_PER_CU_>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WG_PER_CU = WG_PER_CU_;
     static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES_M * WAVES_N / 4;
     static constexpr int LDS_BYTES = 2 * (BM + BN) * (BK + 4) * 4;
 };
 
 template <class Cfg, int EPI>
-__global__ void __launch_bounds__(Cfg::THREADS)
+__global__ void __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD)
 gemm_epi_kernel(GemmArgs a)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WAVES_M = Cfg::WAVES_M, WAVES_N = Cfg::WAVES_N;
@@ -176,35 +179,64 @@ gemm_epi_kernel(GemmArgs a)
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 4;
 
+    // Operand fragments of one 8-deep K group ("sub-step"), double-buffered in
+    // registers so the next group's LDS reads overlap this group's MFMAs.
+    constexpr int G = BK / 8;
+    f32x4 fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, int kk, f32x4 (&af)[FM], f32x4 (&bf)[FN]) {
+        const float *As = smem + buf * STAGE;
+        const float *Bs = As + BM * LDK;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            af[i] = *reinterpret_cast<const f32x4 *>(As + (wm * TM + i * 32 + frag_row) * LDK + kk + frag_k);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bf[j] = *reinterpret_cast<const f32x4 *>(Bs + (wn * TN + j * 32 + frag_row) * LDK + kk + frag_k);
+    };
+    auto mfma_group = [&](const f32x4 (&af)[FM], const f32x4 (&bf)[FN]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][c], bf[j][c], acc[i][j], 0, 0, 0);
+    };
+
+    // Software pipeline over K steps (one LDS stage = BK of K per step):
+    //   * the next step's tile is fetched into registers at the top of a step
+    //     and written to the other LDS stage before the step's last MFMA
+    //     group is issued, so the stores complete under MFMA work;
+    //   * the last group's MFMAs are issued after the barrier, together with
+    //     the LDS reads of the next step's first group, so the matrix pipe
+    //     has queued work while those reads are in flight.
+    // The other stage is free to overwrite: every wavefront finished reading
+    // it before the previous barrier.
     if (nk > 0) {
         gload(kbeg);
         sstore(0);
         __syncthreads();
+        read_frags(0, 0, fa[0], fb[0]);
     }
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
+        const int buf = kt & 1;
         if (more) gload(kbeg + (kt + 1) * BK);
-        const float *As = smem + (kt & 1) * STAGE;
-        const float *Bs = As + BM * LDK;
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 8) {
-            f32x4 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const f32x4 *>(As + (wm * TM + i * 32 + frag_row) * LDK + kk + frag_k);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const f32x4 *>(Bs + (wn * TN + j * 32 + frag_row) * LDK + kk + frag_k);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][c], bf[j][c], acc[i][j], 0, 0, 0);
+        for (int g = 0; g < G - 1; ++g) {
+            read_frags(buf, (g + 1) * 8, fa[(g + 1) & 1], fb[(g + 1) & 1]);
+            if (g == G - 2 && more) sstore(buf ^ 1);
+            mfma_group(fa[g & 1], fb[g & 1]);
         }
-        if (more) sstore((kt + 1) & 1);
+        // Keep the stores and the second-to-last group's MFMAs ahead of the
+        // barrier, and the next step's first LDS reads ahead of the last
+        // group's MFMAs (MFMAs carry no memory dependence, so the scheduler
+        // would otherwise move them across the barrier).
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        if (more) read_frags(buf ^ 1, 0, fa[G & 1], fb[G & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group(fa[(G - 1) & 1], fb[(G - 1) & 1]);
     }
 
     // ------------------------------------------------------------------ epilogue

@@ -19,9 +19,9 @@ namespace {
 //   LARGE  256x256, 8 wavefronts (4x2, 64x128 each), 144 KiB LDS, 1 WG/CU
 //   MID    128x256, 8 wavefronts (2x4, 64x64 each),  108 KiB LDS, 1 WG/CU
 //   SMALL  128x128, 4 wavefronts (2x2, 64x64 each),   72 KiB LDS, 2 WG/CU
-using CfgLarge = TileCfg<256, 256, 32, 4, 2>;
-using CfgMid = TileCfg<128, 256, 32, 2, 4>;
-using CfgSmall = TileCfg<128, 128, 32, 2, 2>;
+using CfgLarge = TileCfg<256, 256, 32, 4, 2, 1>;
+using CfgMid = TileCfg<128, 256, 32, 2, 4, 1>;
+using CfgSmall = TileCfg<128, 128, 32, 2, 2, 2>;
 
 enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_COUNT = 3 };
 
