@@ -98,6 +98,10 @@ def main() -> int:
     ap.add_argument("--split-k", type=int, default=0, help="0 auto, 1 off, S>=2 forced")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused ablation (GEMM to memory, then a separate tail kernel)")
+    ap.add_argument("--pool-fold", action="store_true",
+                    help="tail (b) via window-averaged weights: the GEMM is M x N/16 x K (FLOPs counted as such)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -127,19 +131,38 @@ def main() -> int:
         bd = torch.from_numpy(b).to(dev)
         Y = torch.empty(lib.LinEpi.output_shape(w.M, w.N, tail.kind), dtype=torch.float32, device=dev)
     stream.synchronize()
-    desc = lib.make_desc(tail.kind, tail.scale, tail.lo, tail.hi, tail.pool_kernel)
-
+    ref_tail = tail
     h = lib.LinEpi(stream=stream)
     h.set_option(lib.LIN_EPI_OPT_SPLIT_K, args.split_k)
+    h.set_option(lib.LIN_EPI_OPT_UNFUSED, 1 if args.unfused else 0)
+    flops = float(w.flops)
+    prep_ms = None
+    if args.pool_fold:
+        if tail.kind != workloads.POOL_GELU_SCALE_ROWMAX:
+            print("--pool-fold applies to tail (b) workloads only", file=sys.stderr)
+            return 2
+        # one-time preparation per weight, timed on its own
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            e0.record(stream)
+            Wd_run, bd_run = h.pool_weights(Wd, bd, tail.pool_kernel)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        prep_ms = e0.elapsed_time(e1)
+        tail = workloads.TAIL_B_FOLDED
+        flops = 2.0 * w.M * (w.N // 16) * w.K
+    else:
+        Wd_run, bd_run = Wd, bd
+    desc = lib.make_desc(tail.kind, tail.scale, tail.lo, tail.hi, tail.pool_kernel)
     for _ in range(args.warmup):
-        h.run_into(Xd, Wd, bd, desc, Y)
+        h.run_into(Xd, Wd_run, bd_run, desc, Y)
     torch.cuda.synchronize()
 
     # quick parity spot check of the benchmarked output (4 rows)
     import oracle
 
     rows = workloads.checked_rows(w.M, seed=w.seed)[:4]
-    ref = oracle.forward_rows(X, W, b, tail.kind, rows, **tail.params())
+    ref = oracle.forward_rows(X, W, b, ref_tail.kind, rows, **ref_tail.params())
     got = Y.cpu().numpy().astype(np.float64)[rows]
     spot_err = float(np.max(np.abs(got - ref)))
     spot_ok = bool(np.all(np.abs(got - ref) <= 1e-3 * (1 + np.abs(ref))))
@@ -151,7 +174,7 @@ def main() -> int:
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
-        h.run_into(Xd, Wd, bd, desc, Y)
+        h.run_into(Xd, Wd_run, bd_run, desc, Y)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -168,7 +191,6 @@ def main() -> int:
         del src, dst
 
     ms_per_step = total_ms / args.steps
-    flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = prof.total_ms[0] / max(1, prof.launches[0])
     achieved = flops / (gemm_ms * 1e-3) / 1e12
@@ -194,6 +216,7 @@ def main() -> int:
             "split_k": plan.split_k,
             "kernels_per_step": plan.kernels,
             "frac_of_fp32_mfma_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
+            "variant": "pool_fold" if args.pool_fold else ("unfused" if args.unfused else "fused"),
         },
         "roofline": {
             "bound": "mfma",
@@ -205,9 +228,14 @@ def main() -> int:
             "kernel_ms": round(gemm_ms, 5),
             "launches": int(prof.launches[0]),
             "second_pass_ms": round(prof.total_ms[1] / prof.launches[1], 5) if prof.launches[1] else None,
+            "tail_pass_ms": round(prof.total_ms[2] / prof.launches[2], 5) if prof.launches[2] else None,
         },
         "parity_spot_check": {"rows": 4, "max_abs_err": spot_err, "ok": spot_ok},
     }
+    if args.pool_fold:
+        out["config"]["pool_weights_prep_ms"] = round(prep_ms, 5)
+        out["config"]["gemm_flops_counted"] = "2*M*(N/16)*K"
+        out["config"]["equivalent_unfolded_tflops"] = round(w.flops / (ms_per_step * 1e-3) / 1e12, 3)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, X, W, b, args.cpu_seconds)

@@ -20,6 +20,7 @@ LIN_EPI_NONE = 0
 LIN_EPI_SCALE_HARDTANH_GELU = 1
 LIN_EPI_POOL_GELU_SCALE_ROWMAX = 2
 LIN_EPI_SWISH_SCALE = 3
+LIN_EPI_GELU_SCALE_ROWMAX = 4
 
 # status codes
 LIN_EPI_OK = 0
@@ -32,6 +33,7 @@ LIN_EPI_EHIP = -5
 # options
 LIN_EPI_OPT_SPLIT_K = 1
 LIN_EPI_OPT_PROFILE = 2
+LIN_EPI_OPT_UNFUSED = 3
 
 # every function include/lin_epi.h declares
 EXPORTS = (
@@ -39,8 +41,10 @@ EXPORTS = (
     "lin_epi_run",
     "lin_epi_destroy",
     "lin_epi_status_string",
+    "lin_epi_pool_weights",
     "lin_epi_set_option",
     "lin_epi_last_plan",
+    "lin_epi_query_plan",
     "lin_epi_profile_read",
 )
 
@@ -70,8 +74,8 @@ class lin_epi_plan(ctypes.Structure):
 
 class lin_epi_profile(ctypes.Structure):
     _fields_ = [
-        ("launches", ctypes.c_int64 * 2),
-        ("total_ms", ctypes.c_double * 2),
+        ("launches", ctypes.c_int64 * 3),
+        ("total_ms", ctypes.c_double * 3),
     ]
 
 
@@ -101,10 +105,15 @@ def load_library():
     lib.lin_epi_destroy.restype = ctypes.c_int
     lib.lin_epi_status_string.argtypes = [ctypes.c_int]
     lib.lin_epi_status_string.restype = ctypes.c_char_p
+    lib.lin_epi_pool_weights.argtypes = [p, i64, i64, p, p, i32, p, p]
+    lib.lin_epi_pool_weights.restype = ctypes.c_int
     lib.lin_epi_set_option.argtypes = [p, i32, i64]
     lib.lin_epi_set_option.restype = ctypes.c_int
     lib.lin_epi_last_plan.argtypes = [p, ctypes.POINTER(lin_epi_plan)]
     lib.lin_epi_last_plan.restype = ctypes.c_int
+    lib.lin_epi_query_plan.argtypes = [p, i64, i64, i64, ctypes.POINTER(lin_epi_desc), i32,
+                                       ctypes.POINTER(lin_epi_plan)]
+    lib.lin_epi_query_plan.restype = ctypes.c_int
     lib.lin_epi_profile_read.argtypes = [p, ctypes.POINTER(lin_epi_profile)]
     lib.lin_epi_profile_read.restype = ctypes.c_int
     _lib = lib
@@ -136,6 +145,12 @@ def lin_epi_destroy(handle: int) -> int:
     return load_library().lin_epi_destroy(ctypes.c_void_p(handle or None))
 
 
+def lin_epi_pool_weights(handle: int, N: int, K: int, W: int, b: int, pool_kernel: int, Wp: int, bp: int) -> int:
+    return load_library().lin_epi_pool_weights(ctypes.c_void_p(handle or None), N, K, ctypes.c_void_p(W or None),
+                                               ctypes.c_void_p(b or None), pool_kernel, ctypes.c_void_p(Wp or None),
+                                               ctypes.c_void_p(bp or None))
+
+
 def lin_epi_set_option(handle: int, option: int, value: int) -> int:
     return load_library().lin_epi_set_option(ctypes.c_void_p(handle or None), option, value)
 
@@ -143,6 +158,14 @@ def lin_epi_set_option(handle: int, option: int, value: int) -> int:
 def lin_epi_last_plan(handle: int) -> tuple[int, lin_epi_plan]:
     p = lin_epi_plan()
     rc = load_library().lin_epi_last_plan(ctypes.c_void_p(handle or None), ctypes.byref(p))
+    return rc, p
+
+
+def lin_epi_query_plan(handle: int, M: int, N: int, K: int, desc: lin_epi_desc | None,
+                       num_cus: int) -> tuple[int, lin_epi_plan]:
+    p = lin_epi_plan()
+    d = ctypes.byref(desc) if desc is not None else None
+    rc = load_library().lin_epi_query_plan(ctypes.c_void_p(handle or None), M, N, K, d, num_cus, ctypes.byref(p))
     return rc, p
 
 
@@ -211,7 +234,20 @@ class LinEpi:
 
     @staticmethod
     def output_shape(M: int, N: int, kind: int) -> tuple:
-        return (M,) if kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX else (M, N)
+        return (M,) if kind in (LIN_EPI_POOL_GELU_SCALE_ROWMAX, LIN_EPI_GELU_SCALE_ROWMAX) else (M, N)
+
+    def pool_weights(self, W, b, pool_kernel: int = 16):
+        """Window-averaged weights and bias (device tensors) for tail (b)."""
+        import torch
+
+        N, K = W.shape
+        L = N // pool_kernel
+        Wp = torch.empty((L, K), dtype=torch.float32, device=W.device)
+        bp = torch.empty((L,), dtype=torch.float32, device=W.device)
+        rc = lin_epi_pool_weights(self.handle, N, K, W.data_ptr(), b.data_ptr(), pool_kernel, Wp.data_ptr(),
+                                  bp.data_ptr())
+        _check(rc, "lin_epi_pool_weights")
+        return Wp, bp
 
     def run_into(self, X, W, b, desc: lin_epi_desc, Y) -> None:
         M, K = X.shape

@@ -45,6 +45,7 @@ enum EpiKind : int {
     EPI_POOL_GELU_SCALE_ROWMAX = 2,
     EPI_SWISH_SCALE = 3,
     EPI_SPLITK_PARTIAL = 4,  // raw partial sums of one K slice, no bias/tail
+    EPI_GELU_SCALE_ROWMAX = 5,  // max over columns of scale*GELU(y): tail (b) on pooled weights
 };
 
 struct GemmArgs {
@@ -256,13 +257,16 @@ gemm_epi_kernel(GemmArgs a)
                     if (m < M && n < N) P[(int64_t)m * N + n] = acc[i][j][r];
                 }
         }
-    } else if constexpr (EPI == EPI_POOL_GELU_SCALE_ROWMAX) {
-        // AvgPool1d(16): a 16-wide window is 16 consecutive columns, i.e. the
-        // 16 lanes of one quarter-wavefront holding the same row; sum them
-        // with butterfly shuffles.  Window j is kept only if it lies wholly
-        // inside N (floor mode).  Then GELU, scale, and the max over this
-        // workgroup's windows of each row; the max over column tiles is done
-        // by a second, deterministic pass.
+    } else if constexpr (EPI == EPI_POOL_GELU_SCALE_ROWMAX || EPI == EPI_GELU_SCALE_ROWMAX) {
+        // Row maximum of scale*GELU over this workgroup's columns, one partial
+        // per (row, column tile); a second pass takes the max over tiles.
+        // With pooling (AvgPool1d(16)): a 16-wide window is 16 consecutive
+        // columns, i.e. the 16 lanes of one quarter-wavefront holding the same
+        // row; they are summed with butterfly shuffles, and window j is kept
+        // only if it lies wholly inside N (floor mode).  Without pooling (the
+        // pooled-weight variant, whose columns already are window means) every
+        // column < N is a candidate.
+        constexpr bool POOL = EPI == EPI_POOL_GELU_SCALE_ROWMAX;
         const int L = N >> 4;
         float bn[FN];
         bool win_ok[FN];
@@ -270,7 +274,7 @@ gemm_epi_kernel(GemmArgs a)
         for (int j = 0; j < FN; ++j) {
             const int n = n0 + wn * TN + j * 32 + col_in_block;
             bn[j] = n < N ? a.bias[n] : 0.f;
-            win_ok[j] = ((n0 + wn * TN + j * 32 + (col_in_block & 16)) >> 4) < L;
+            win_ok[j] = POOL ? ((n0 + wn * TN + j * 32 + (col_in_block & 16)) >> 4) < L : n < N;
         }
         __syncthreads();  // LDS stages are free now; reuse them for the cross-wave max
         float *red = smem;  // [WAVES_N][BM]
@@ -282,12 +286,21 @@ gemm_epi_kernel(GemmArgs a)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     float v = acc[i][j][r] + bn[j];
-                    v += __shfl_xor(v, 1);
-                    v += __shfl_xor(v, 2);
-                    v += __shfl_xor(v, 4);
-                    v += __shfl_xor(v, 8);
-                    const float g = gelu_erf(v * 0.0625f) * a.tail.scale;
+                    if constexpr (POOL) {
+                        v += __shfl_xor(v, 1);
+                        v += __shfl_xor(v, 2);
+                        v += __shfl_xor(v, 4);
+                        v += __shfl_xor(v, 8);
+                        v *= 0.0625f;
+                    }
+                    const float g = gelu_erf(v) * a.tail.scale;
                     mx = fmaxf(mx, win_ok[j] ? g : -INFINITY);
+                }
+                if constexpr (!POOL) {
+                    mx = fmaxf(mx, __shfl_xor(mx, 1));
+                    mx = fmaxf(mx, __shfl_xor(mx, 2));
+                    mx = fmaxf(mx, __shfl_xor(mx, 4));
+                    mx = fmaxf(mx, __shfl_xor(mx, 8));
                 }
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 if ((lane & 31) == 0) red[wn * BM + wm * TM + i * 32 + (r >> 2) * 8 + row_half + (r & 3)] = mx;
@@ -324,19 +337,102 @@ gemm_epi_kernel(GemmArgs a)
 
 // Second pass of split-K: Y[m,n] = tail(sum_{s=0..S-1} P[s,m,n] + b[n]), the
 // slices added in increasing s, so the result is the same on every run.
+// With vec4 (N % 4 == 0 and Y 16-byte aligned; the workspace always is) each
+// thread handles four consecutive columns of one row with 128-bit accesses.
 template <int EPI>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *P, const float *bias, float *Y,
-                                                            int64_t MN, int32_t N, int32_t S, TailParams tail)
+                                                            int64_t MN, int32_t N, int32_t S, TailParams tail,
+                                                            int32_t vec4)
 {
     using Tail = typename std::conditional<
         EPI == EPI_SCALE_HARDTANH_GELU, TailScaleHardtanhGelu,
         typename std::conditional<EPI == EPI_SWISH_SCALE, TailSwishScale, TailNone>::type>::type;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += stride) {
-        float s = P[e];
-        for (int k = 1; k < S; ++k) s += P[(int64_t)k * MN + e];
-        Y[e] = Tail::apply(s + bias[e % N], tail);
+    int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (vec4) {
+        for (; e < MN / 4; e += stride) {
+            f32x4 v = reinterpret_cast<const f32x4 *>(P)[e];
+            for (int k = 1; k < S; ++k) v += reinterpret_cast<const f32x4 *>(P + (int64_t)k * MN)[e];
+            const int n = (int)((e * 4) % N);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = Tail::apply(v[c] + bias[n + c], tail);
+            reinterpret_cast<f32x4 *>(Y)[e] = v;
+        }
+    } else {
+        for (; e < MN; e += stride) {
+            float v = P[e];
+            for (int k = 1; k < S; ++k) v += P[(int64_t)k * MN + e];
+            Y[e] = Tail::apply(v + bias[e % N], tail);
+        }
     }
+}
+
+// Row-max pass over materialised sums, one workgroup (256 threads) per row m:
+// y[n] = sum_{s=0..S-1} P[s, m, n] (+ b[n] when bias is given), slices added
+// in order; windows of `pool` consecutive columns averaged (pool = 16:
+// AvgPool1d(16), floor mode; pool = 1: every column); Y[m] = max_j scale *
+// GELU(window j).  Used as the second pass of split-K for the row-max tails
+// (S slices, bias) and as the tail pass of the unfused ablation (S = 1, the
+// raw output already holds the bias).  Lane t of a 256-column chunk owns
+// column n0 + t, so every load is coalesced; a 16-wide window is 16
+// consecutive lanes (chunks start at multiples of 16) and is summed with
+// butterfly shuffles.
+// With vec4 (N % 4 == 0 and P 16-byte aligned) a lane owns four consecutive
+// columns instead, loaded with 128-bit reads, and a window is 4 lanes.
+__global__ void __launch_bounds__(256) rowmax_pass_kernel(const float *P, const float *bias, float *Y, int64_t MN,
+                                                          int32_t N, int32_t S, int32_t pool, float scale,
+                                                          int32_t vec4)
+{
+    __shared__ float red[4];
+    const int64_t row = (int64_t)blockIdx.x * N;
+    const int ncols = (N / pool) * pool;  // columns that belong to a whole window
+    float mx = -INFINITY;
+    if (vec4) {
+        for (int n0 = 0; n0 < ncols; n0 += 1024) {
+            const int n = n0 + 4 * (int)threadIdx.x;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (n < ncols) {
+                v = *reinterpret_cast<const f32x4 *>(P + row + n);
+                for (int k = 1; k < S; ++k) v += *reinterpret_cast<const f32x4 *>(P + (int64_t)k * MN + row + n);
+                if (bias) {
+                    v[0] += bias[n];
+                    v[1] += bias[n + 1];
+                    v[2] += bias[n + 2];
+                    v[3] += bias[n + 3];
+                }
+            }
+            if (pool == 16) {
+                float w = (v[0] + v[1]) + (v[2] + v[3]);
+                w += __shfl_xor(w, 1);
+                w += __shfl_xor(w, 2);
+                if (n < ncols) mx = fmaxf(mx, gelu_erf(w * 0.0625f) * scale);
+            } else if (n < ncols) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) mx = fmaxf(mx, gelu_erf(v[c]) * scale);
+            }
+        }
+    }
+    for (int n0 = 0; !vec4 && n0 < ncols; n0 += 256) {
+        const int n = n0 + (int)threadIdx.x;
+        float v = 0.f;
+        if (n < ncols) {
+            v = P[row + n];
+            for (int k = 1; k < S; ++k) v += P[(int64_t)k * MN + row + n];
+            if (bias) v += bias[n];
+        }
+        if (pool == 16) {
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 8);
+            v *= 0.0625f;
+        }
+        if (n < ncols) mx = fmaxf(mx, gelu_erf(v) * scale);
+    }
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) Y[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // Second pass of tail (b): Y[m] = max over column tiles of the per-tile row
@@ -350,6 +446,62 @@ __global__ void __launch_bounds__(256) rowmax_finalize_kernel(const float *part,
     float v = p[0];
     for (int t = 1; t < tiles_n; ++t) v = fmaxf(v, p[t]);
     Y[m] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Unfused tail kernels: the same tails as separate passes over a materialised
+// linear output, as the pages' own solutions run them after a library GEMM.
+// They exist to measure what fusing the tail into the GEMM epilogue saves.
+
+// Y[e] = tail(Y[e]) in place, four elements per thread when Y is 16-byte
+// aligned and the length is a multiple of 4, else one.
+template <int EPI>
+__global__ void __launch_bounds__(256) tail_inplace_kernel(float *Y, int64_t count, TailParams tail, int vec4)
+{
+    using Tail = typename std::conditional<
+        EPI == EPI_SCALE_HARDTANH_GELU, TailScaleHardtanhGelu,
+        typename std::conditional<EPI == EPI_SWISH_SCALE, TailSwishScale, TailNone>::type>::type;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (vec4) {
+        f32x4 *Y4 = reinterpret_cast<f32x4 *>(Y);
+        for (; e < count / 4; e += stride) {
+            f32x4 v = Y4[e];
+            v[0] = Tail::apply(v[0], tail);
+            v[1] = Tail::apply(v[1], tail);
+            v[2] = Tail::apply(v[2], tail);
+            v[3] = Tail::apply(v[3], tail);
+            Y4[e] = v;
+        }
+    } else {
+        for (; e < count; e += stride) Y[e] = Tail::apply(Y[e], tail);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pooled weights for tail (b): W_p[j, :] = mean over the `pool` rows
+// j*pool .. j*pool+pool-1 of W, b_p[j] = mean of the same bias entries, for
+// j < floor(N / pool).  Rows are added in increasing order, then scaled by
+// 1/pool.  One-dimensional grid of L * chunks workgroups: workgroup w handles
+// pooled row w / chunks and 256 float4 columns starting at (w % chunks)*256.
+// HBM-bound.
+__global__ void __launch_bounds__(256) pool_weights_kernel(const float *W, const float *b, float *Wp, float *bp,
+                                                           int64_t K, int32_t pool, int32_t chunks)
+{
+    const int64_t j = blockIdx.x / chunks;
+    const int64_t c4 = (int64_t)(blockIdx.x % chunks) * blockDim.x + threadIdx.x;
+    const float inv = 1.0f / (float)pool;
+    if (c4 * 4 < K) {
+        const float *src = W + (int64_t)j * pool * K + c4 * 4;
+        f32x4 s = *reinterpret_cast<const f32x4 *>(src);
+        for (int t = 1; t < pool; ++t) s += *reinterpret_cast<const f32x4 *>(src + (int64_t)t * K);
+        *reinterpret_cast<f32x4 *>(Wp + (int64_t)j * K + c4 * 4) = s * inv;
+    }
+    if (blockIdx.x % chunks == 0 && threadIdx.x == 0) {
+        float s = b[(int64_t)j * pool];
+        for (int t = 1; t < pool; ++t) s += b[(int64_t)j * pool + t];
+        bp[j] = s * inv;
+    }
 }
 
 }  // namespace lin_epi

@@ -3,6 +3,7 @@
 // timing.  Kernels live in gemm_mfma.hpp and epilogue.hpp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -54,6 +55,7 @@ struct lin_epi_ctx {
     size_t ws_bytes = 0;
     int64_t split_opt = 0;
     bool profile = false;
+    bool unfused = false;
     bool has_plan = false;
     lin_epi_plan plan{};
     std::vector<PendingTiming> pending;
@@ -132,9 +134,12 @@ template <int EPI>
 void launch_reduce(const float *P, const float *bias, float *Y, int64_t MN, int N, int S, TailParams t,
                    hipStream_t s)
 {
-    int64_t blocks = (MN + 255) / 256;
+    const int32_t vec4 = (N % 4 == 0) && (((uintptr_t)Y & 15u) == 0) && (((uintptr_t)P & 15u) == 0);
+    int64_t blocks = ((vec4 ? MN / 4 : MN) + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, s, P, bias, Y, MN, N, S, t);
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, s, P, bias, Y, MN, N, S, t,
+                       vec4);
 }
 
 struct Plan {
@@ -152,9 +157,10 @@ struct Plan {
 // run tiles*S workgroups on this device, and reduce_cost is the second pass
 // relative to the GEMM: S partial reads plus one output write of M*N floats
 // at ~4 TB/s against 2*M*N*K FLOP at ~120 TFLOP/s, i.e. (S + 1) * 60 / K.
-// A slice keeps at least 8 K steps.  Tail (b) never splits (its pooling and
-// row max act on complete sums).  LIN_EPI_OPT_SPLIT_K overrides S.
-Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind)
+// A slice keeps at least 8 K steps.  LIN_EPI_OPT_SPLIT_K overrides S.  For
+// the row-max tails a split moves pooling, GELU and the max into the second
+// pass, which reads complete sums.
+Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int num_cus)
 {
     Plan best{CFG_SMALL, 1, 0, 0, 0};
     double best_score = -1.0;
@@ -163,14 +169,15 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
         const int64_t tm = (M + ci.bm - 1) / ci.bm, tn = (N + ci.bn - 1) / ci.bn;
         const int64_t tiles = tm * tn;
         const double useful = (double)M * (double)N / ((double)tm * ci.bm * (double)tn * ci.bn);
-        const int64_t slots = (int64_t)h->num_cus * ci.wgs_per_cu;
+        const int64_t slots = (int64_t)num_cus * ci.wgs_per_cu;
         const int64_t steps = (K + ci.bk - 1) / ci.bk;
-        int s_lo = 1, s_hi = 8;
-        if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX || h->split_opt == 1) s_hi = 1;
-        if (h->split_opt >= 2) s_lo = s_hi = (int)h->split_opt;
+        // A forced split is clamped to the K steps available, so every slice
+        // owns at least one; the first candidate (S = s_lo) is always scored.
+        int s_lo = 1, s_hi = 16;
+        if (h->split_opt == 1) s_hi = 1;
+        if (h->split_opt >= 2) s_lo = s_hi = (int)std::min<int64_t>(h->split_opt, std::max<int64_t>(steps, 1));
         for (int S = s_lo; S <= s_hi; ++S) {
-            if (S > 1 && h->split_opt < 2 && steps < 8 * S) break;
-            if (S > 1 && S > steps) break;
+            if (S > s_lo && steps < 8 * S) break;
             const int64_t units = tiles * S;
             const int64_t rounds = (units + slots - 1) / slots;
             const double balance = (double)units / (double)(rounds * slots);
@@ -193,6 +200,63 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
         best.k_slice = steps > 0 ? steps * ci.bk : ci.bk;
     }
     return best;
+}
+
+bool is_rowmax(int kind)
+{
+    return kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX || kind == LIN_EPI_GELU_SCALE_ROWMAX;
+}
+
+// The launch plan of one lin_epi_run call: tile configuration and K slices
+// from choose_plan, then the kernels the chosen path launches and the
+// workspace it needs.
+//   fused, no split:       GEMM+tail (1 kernel); row-max kinds add the
+//                          finalize pass and M*tiles_n partial maxima
+//   fused, split S:        GEMM partials [S,M,N] + second pass (2 kernels)
+//   unfused ablation:      GEMM (+ reduce if split) to raw y, then a tail
+//                          kernel (none for kind 0); raw y for the row-max
+//                          kinds lives in the workspace after the partials
+lin_epi_plan describe(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, int kind)
+{
+    lin_epi_plan p{};
+    p.tile_m = kCfgs[pl.cfg].bm;
+    p.tile_n = kCfgs[pl.cfg].bn;
+    p.tile_k = kCfgs[pl.cfg].bk;
+    p.split_k = pl.split;
+    p.grid_main = (int64_t)pl.tiles_m * pl.tiles_n * pl.split;
+    const int64_t MN = M * N;
+    const int64_t partials = pl.split > 1 ? (int64_t)pl.split * MN : 0;
+    if (h->unfused) {
+        p.kernels = (pl.split > 1 ? 2 : 1) + (kind != LIN_EPI_NONE ? 1 : 0);
+        p.workspace_bytes = (partials + (is_rowmax(kind) ? MN : 0)) * (int64_t)sizeof(float);
+    } else if (pl.split > 1) {
+        p.kernels = 2;
+        p.workspace_bytes = partials * (int64_t)sizeof(float);
+    } else if (is_rowmax(kind)) {
+        p.kernels = 2;
+        p.workspace_bytes = M * pl.tiles_n * (int64_t)sizeof(float);
+    } else {
+        p.kernels = 1;
+        p.workspace_bytes = 0;
+    }
+    return p;
+}
+
+// Host-side argument checks shared by lin_epi_run and lin_epi_query_plan.
+int validate_desc(int64_t M, int64_t N, int64_t K, const lin_epi_desc *desc)
+{
+    if (!desc) return LIN_EPI_EINVAL;
+    if (M < 0 || N < 0 || K < 0) return LIN_EPI_EINVAL;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return LIN_EPI_EINVAL;
+    const int kind = desc->kind;
+    if (kind < LIN_EPI_NONE || kind > LIN_EPI_GELU_SCALE_ROWMAX) return LIN_EPI_EINVAL;
+    if (kind == LIN_EPI_SCALE_HARDTANH_GELU && !(desc->ht_min <= desc->ht_max)) return LIN_EPI_EINVAL;
+    if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX) {
+        if (desc->pool_kernel != 16 || desc->pool_stride != desc->pool_kernel) return LIN_EPI_ENOTSUP;
+        if (N > 0 && N < 16) return LIN_EPI_ENOTSUP;
+    }
+    if (K % 4 != 0) return LIN_EPI_EALIGN;
+    return LIN_EPI_OK;
 }
 
 }  // namespace
@@ -251,6 +315,10 @@ int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value)
             if (value != 0 && value != 1) return LIN_EPI_EINVAL;
             h->profile = value != 0;
             return LIN_EPI_OK;
+        case LIN_EPI_OPT_UNFUSED:
+            if (value != 0 && value != 1) return LIN_EPI_EINVAL;
+            h->unfused = value != 0;
+            return LIN_EPI_OK;
         default: return LIN_EPI_EINVAL;
     }
 }
@@ -291,31 +359,28 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
                 const lin_epi_desc *desc, float *Y)
 {
     // ---- validation: host only, before any HIP call
-    if (!h || !desc) return LIN_EPI_EINVAL;
-    if (M < 0 || N < 0 || K < 0) return LIN_EPI_EINVAL;
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return LIN_EPI_EINVAL;
-    const int kind = desc->kind;
-    if (kind < LIN_EPI_NONE || kind > LIN_EPI_SWISH_SCALE) return LIN_EPI_EINVAL;
-    if (kind == LIN_EPI_SCALE_HARDTANH_GELU && !(desc->ht_min <= desc->ht_max)) return LIN_EPI_EINVAL;
-    if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX) {
-        if (desc->pool_kernel != 16 || desc->pool_stride != desc->pool_kernel) return LIN_EPI_ENOTSUP;
-        if (N > 0 && N < 16) return LIN_EPI_ENOTSUP;
-    }
+    if (!h) return LIN_EPI_EINVAL;
+    int rc = validate_desc(M, N, K, desc);
+    if (rc != LIN_EPI_OK && rc != LIN_EPI_EALIGN) return rc;
     if (M == 0 || N == 0) return LIN_EPI_OK;
     if (!b || !Y) return LIN_EPI_EINVAL;
     if (K > 0 && (!X || !W)) return LIN_EPI_EINVAL;
-    if (K % 4 != 0) return LIN_EPI_EALIGN;
+    if (rc != LIN_EPI_OK) return rc;
     if (K > 0 && (((uintptr_t)X | (uintptr_t)W) & 15u)) return LIN_EPI_EALIGN;
     if (((uintptr_t)Y | (uintptr_t)b) & 3u) return LIN_EPI_EALIGN;
+    const int kind = desc->kind;
 
-    int rc = ensure_device(h);
+    rc = ensure_device(h);
     if (rc != LIN_EPI_OK) return rc;
 
-    const Plan pl = choose_plan(h, M, N, K, kind);
+    const bool rowmax = is_rowmax(kind);
+    const bool unfused = h->unfused;
+    const Plan pl = choose_plan(h, M, N, K, h->num_cus);
     const int tiles_m = pl.tiles_m, tiles_n = pl.tiles_n;
     const int64_t tiles = (int64_t)tiles_m * tiles_n;
     const int split = pl.split;
-    const int64_t k_slice = pl.k_slice;
+    const int64_t MN = M * N;
+    lin_epi_plan plan = describe(h, pl, M, N, kind);
 
     GemmArgs g{};
     g.X = X;
@@ -324,25 +389,43 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
     g.M = (int32_t)M;
     g.N = (int32_t)N;
     g.K = (int32_t)K;
-    g.k_slice = (int32_t)k_slice;
+    g.k_slice = (int32_t)pl.k_slice;
     g.tiles_m = tiles_m;
     g.tiles_n = tiles_n;
     g.tail = TailParams{desc->scale, desc->ht_min, desc->ht_max};
 
-    lin_epi_plan plan{};
-    plan.tile_m = kCfgs[pl.cfg].bm;
-    plan.tile_n = kCfgs[pl.cfg].bn;
-    plan.tile_k = kCfgs[pl.cfg].bk;
-    plan.split_k = split;
-    plan.grid_main = tiles * split;
-
     hipStream_t s = h->stream;
-    if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX) {
+    if (!unfused && rowmax && split > 1) {
+        // Split-K partial sums -> one pass that adds the slices in order,
+        // adds the bias, pools, applies GELU and the scale and takes the max.
+        const size_t bytes = (size_t)split * MN * sizeof(float);
+        rc = ensure_workspace(h, bytes);
+        if (rc != LIN_EPI_OK) return rc;
+        g.out = static_cast<float *>(h->ws);
+        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s); });
+        if (rc != LIN_EPI_OK) return rc;
+        const float *P = static_cast<const float *>(h->ws);
+        const int32_t pool = kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1;
+        const float scale = desc->scale;
+        const int32_t Ni = (int32_t)N;
+        rc = timed_launch(h, 1, [&] {
+            hipLaunchKernelGGL(rowmax_pass_kernel, dim3((unsigned)M), dim3(256), 0, s, P, b, Y, MN, Ni, split, pool,
+                               scale, (int32_t)(N % 4 == 0));
+        });
+        if (rc != LIN_EPI_OK) return rc;
+    } else if (!unfused && rowmax) {
+        // GEMM with the row-max epilogue -> per-(row, column tile) partials ->
+        // deterministic max over column tiles.
         const size_t bytes = (size_t)M * tiles_n * sizeof(float);
         rc = ensure_workspace(h, bytes);
         if (rc != LIN_EPI_OK) return rc;
         g.out = static_cast<float *>(h->ws);
-        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s); });
+        rc = timed_launch(h, 0, [&] {
+            if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX)
+                launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s);
+            else
+                launch_gemm<EPI_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s);
+        });
         if (rc != LIN_EPI_OK) return rc;
         const float *part = static_cast<const float *>(h->ws);
         const int32_t Mi = (int32_t)M;
@@ -351,17 +434,14 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
                                (int32_t)tiles_n);
         });
         if (rc != LIN_EPI_OK) return rc;
-        plan.kernels = 2;
-        plan.workspace_bytes = (int64_t)bytes;
-    } else if (split > 1) {
-        const size_t bytes = (size_t)split * M * N * sizeof(float);
+    } else if (!unfused && split > 1) {
+        const size_t bytes = (size_t)split * MN * sizeof(float);
         rc = ensure_workspace(h, bytes);
         if (rc != LIN_EPI_OK) return rc;
         g.out = static_cast<float *>(h->ws);
         rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s); });
         if (rc != LIN_EPI_OK) return rc;
         const float *P = static_cast<const float *>(h->ws);
-        const int64_t MN = M * N;
         rc = timed_launch(h, 1, [&] {
             switch (kind) {
                 case LIN_EPI_NONE: launch_reduce<EPI_NONE>(P, b, Y, MN, (int)N, split, g.tail, s); break;
@@ -372,9 +452,7 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
             }
         });
         if (rc != LIN_EPI_OK) return rc;
-        plan.kernels = 2;
-        plan.workspace_bytes = (int64_t)bytes;
-    } else {
+    } else if (!unfused) {
         g.out = Y;
         rc = timed_launch(h, 0, [&] {
             switch (kind) {
@@ -384,12 +462,103 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
             }
         });
         if (rc != LIN_EPI_OK) return rc;
-        plan.kernels = 1;
-        plan.workspace_bytes = 0;
+    } else {
+        // Unfused ablation: raw y = XW^T + b to memory (Y itself for the
+        // elementwise kinds, the workspace for the row-max kinds), then the
+        // tail as a separate pass.  Workspace: [split partials][raw y].
+        const size_t part_floats = split > 1 ? (size_t)split * MN : 0;
+        const size_t raw_floats = rowmax ? (size_t)MN : 0;
+        const size_t bytes = (part_floats + raw_floats) * sizeof(float);
+        if (bytes) {
+            rc = ensure_workspace(h, bytes);
+            if (rc != LIN_EPI_OK) return rc;
+        }
+        float *ws = static_cast<float *>(h->ws);
+        float *Yraw = rowmax ? ws + part_floats : Y;
+        if (split > 1) {
+            g.out = ws;
+            rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s); });
+            if (rc != LIN_EPI_OK) return rc;
+            rc = timed_launch(h, 1, [&] { launch_reduce<EPI_NONE>(ws, b, Yraw, MN, (int)N, split, g.tail, s); });
+            if (rc != LIN_EPI_OK) return rc;
+        } else {
+            g.out = Yraw;
+            rc = timed_launch(h, 0, [&] { launch_gemm<EPI_NONE>(pl.cfg, g, tiles, 1, s); });
+            if (rc != LIN_EPI_OK) return rc;
+        }
+        if (rowmax) {
+            const int32_t pool = kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1;
+            const float scale = desc->scale;
+            const int32_t Ni = (int32_t)N;
+            rc = timed_launch(h, 2, [&] {
+                hipLaunchKernelGGL(rowmax_pass_kernel, dim3((unsigned)M), dim3(256), 0, s, Yraw, (const float *)nullptr,
+                                   Y, MN, Ni, 1, pool, scale,
+                                   (int32_t)(N % 4 == 0 && ((uintptr_t)Yraw & 15u) == 0));
+            });
+        } else if (kind != LIN_EPI_NONE) {
+            const int vec4 = (MN % 4 == 0) && (((uintptr_t)Y & 15u) == 0);
+            int64_t blocks = ((vec4 ? MN / 4 : MN) + 255) / 256;
+            if (blocks > 65536) blocks = 65536;
+            if (blocks < 1) blocks = 1;
+            const TailParams t = g.tail;
+            rc = timed_launch(h, 2, [&] {
+                if (kind == LIN_EPI_SCALE_HARDTANH_GELU)
+                    hipLaunchKernelGGL((tail_inplace_kernel<EPI_SCALE_HARDTANH_GELU>), dim3((unsigned)blocks),
+                                       dim3(256), 0, s, Y, MN, t, vec4);
+                else
+                    hipLaunchKernelGGL((tail_inplace_kernel<EPI_SWISH_SCALE>), dim3((unsigned)blocks), dim3(256), 0,
+                                       s, Y, MN, t, vec4);
+            });
+        }
+        if (rc != LIN_EPI_OK) return rc;
     }
     h->plan = plan;
     h->has_plan = true;
     return LIN_EPI_OK;
+}
+
+int lin_epi_query_plan(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const lin_epi_desc *desc,
+                       int32_t num_cus, lin_epi_plan *out)
+{
+    if (!h || !out || num_cus < 0) return LIN_EPI_EINVAL;
+    const int rc = validate_desc(M, N, K, desc);
+    if (rc != LIN_EPI_OK) return rc;
+    if (num_cus == 0) {
+        const int drc = ensure_device(h);
+        if (drc != LIN_EPI_OK) return drc;
+        num_cus = h->num_cus;
+    }
+    *out = lin_epi_plan{};
+    if (M == 0 || N == 0) return LIN_EPI_OK;
+    const Plan pl = choose_plan(h, M, N, K, num_cus);
+    *out = describe(h, pl, M, N, desc->kind);
+    return LIN_EPI_OK;
+}
+
+int lin_epi_pool_weights(lin_epi_handle h, int64_t N, int64_t K, const float *W, const float *b, int32_t pool_kernel,
+                         float *Wp, float *bp)
+{
+    if (!h) return LIN_EPI_EINVAL;
+    if (N < 0 || K < 0 || pool_kernel < 1) return LIN_EPI_EINVAL;
+    if (N > INT32_MAX || K > INT32_MAX) return LIN_EPI_EINVAL;
+    const int64_t L = N / pool_kernel;
+    if (L == 0) return LIN_EPI_OK;
+    if (!b || !bp) return LIN_EPI_EINVAL;
+    if (K > 0 && (!W || !Wp)) return LIN_EPI_EINVAL;
+    if (K % 4 != 0) return LIN_EPI_EALIGN;
+    if (K > 0 && (((uintptr_t)W | (uintptr_t)Wp) & 15u)) return LIN_EPI_EALIGN;
+    if (((uintptr_t)b | (uintptr_t)bp) & 3u) return LIN_EPI_EALIGN;
+    int rc = ensure_device(h);
+    if (rc != LIN_EPI_OK) return rc;
+    int64_t chunks = (K / 4 + 255) / 256;
+    if (chunks < 1) chunks = 1;
+    if (L * chunks > INT32_MAX) return LIN_EPI_EINVAL;
+    hipStream_t s = h->stream;
+    const int32_t ci = (int32_t)chunks;
+    return timed_launch(h, 2, [&] {
+        hipLaunchKernelGGL(pool_weights_kernel, dim3((unsigned)(L * chunks)), dim3(256), 0, s, W, b, Wp, bp, K,
+                           pool_kernel, ci);
+    });
 }
 
 }  // extern "C"

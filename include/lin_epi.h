@@ -14,6 +14,12 @@
  *       model (Linear, AvgPool1d defaults, GELU, scale, max over dim 1).
  *   kind 3, swish y * sigmoid(y) -> scale
  *       page "Kimi-K2.6 l2_p59", problem analysis (swish, then scaling).
+ *   kind 4, exact-erf GELU -> scale -> max over the output features, with no
+ *       pooling: tail (b) applied to a layer whose weights were already
+ *       averaged per window (lin_epi_pool_weights), the pooled-weight form
+ *       page "Kimi-K2.6 l2_p98" derives (pooling a linear layer's output
+ *       equals a linear layer with window-averaged weights and bias) and
+ *       adopts for its final module.
  *   kind 0, no tail (the plain linear layer), for tests.
  *
  * GELU is 0.5 * x * (1 + erf(x / sqrt 2)) (PyTorch's default form, which
@@ -24,7 +30,7 @@
  * current HIP device, owned by the caller, row-major and densely packed:
  *   X [M, K], W [N, K] (each output feature's weights K-contiguous, the
  *   nn.Linear weight layout), b [N], Y [M, N] for kinds 0, 1, 3 and Y [M]
- *   for kind 2.
+ *   for kinds 2 and 4.
  * X and W must be 16-byte aligned and K a multiple of 4 (rows are read with
  * 128-bit loads); Y must be 4-byte aligned.  Y must not alias X, W or b.
  *
@@ -54,13 +60,14 @@ typedef enum {
     LIN_EPI_NONE = 0,                   /* Y = X W^T + b */
     LIN_EPI_SCALE_HARDTANH_GELU = 1,    /* Y = GELU(clamp((XW^T+b)*scale, ht_min, ht_max)) */
     LIN_EPI_POOL_GELU_SCALE_ROWMAX = 2, /* Y[m] = max_j scale*GELU(mean_{t<16} y[m,16j+t]) */
-    LIN_EPI_SWISH_SCALE = 3             /* Y = (y * sigmoid(y)) * scale */
+    LIN_EPI_SWISH_SCALE = 3,            /* Y = (y * sigmoid(y)) * scale */
+    LIN_EPI_GELU_SCALE_ROWMAX = 4       /* Y[m] = max_n scale*GELU(y[m,n]) */
 } lin_epi_kind;
 
 /* Tail parameters.  Fields a kind does not use are ignored. */
 typedef struct {
     int32_t kind;        /* lin_epi_kind */
-    float scale;         /* kinds 1, 2, 3 */
+    float scale;         /* kinds 1, 2, 3, 4 */
     float ht_min;        /* kind 1: Hardtanh lower bound (inclusive clamp) */
     float ht_max;        /* kind 1: Hardtanh upper bound, ht_min <= ht_max */
     int32_t pool_kernel; /* kind 2: must be 16 */
@@ -69,7 +76,8 @@ typedef struct {
 
 enum {
     LIN_EPI_OK = 0,
-    LIN_EPI_EINVAL = -1,  /* null handle/pointer/desc, negative size, unknown kind, ht_min > ht_max */
+    LIN_EPI_EINVAL = -1,  /* null handle/pointer/desc, negative size, unknown kind, ht_min > ht_max,
+                             pool_kernel < 1 */
     LIN_EPI_EALIGN = -2,  /* X or W not 16-byte aligned, K % 4 != 0, Y not 4-byte aligned */
     LIN_EPI_ENOTSUP = -3, /* kind 2 with pool_kernel != 16, pool_stride != pool_kernel, or N < 16 */
     LIN_EPI_ENOMEM = -4,  /* workspace allocation failed */
@@ -95,16 +103,38 @@ int lin_epi_destroy(lin_epi_handle h);
 /* Static string for a status code. */
 const char *lin_epi_status_string(int status);
 
+/* Window-averaged weights for tail (b), once per weight (page "Kimi-K2.6
+ * l2_p98": the pooled weight and bias are precomputed at construction and
+ * the forward pass is a linear layer with them, followed by GELU, scale and
+ * the row max).  With L = floor(N / pool_kernel):
+ *   Wp[j, k] = (1/pool_kernel) * sum_{t<pool_kernel} W[j*pool_kernel + t, k],
+ *   bp[j]    = (1/pool_kernel) * sum_{t<pool_kernel} b[j*pool_kernel + t],
+ * the rows added in increasing t.  W [N, K], b [N] in; Wp [L, K], bp [L] out,
+ * all device pointers owned by the caller; W and Wp 16-byte aligned, K a
+ * multiple of 4.  Then lin_epi_run(h, M, L, K, X, Wp, bp, desc with kind 4,
+ * Y) gives tail (b) of the original layer up to fp32 rounding, with a GEMM
+ * pool_kernel times smaller.  Enqueued on the handle's stream.  L == 0 is a
+ * no-op.  Errors as lin_epi_run (EINVAL, EALIGN, EHIP). */
+int lin_epi_pool_weights(lin_epi_handle h, int64_t N, int64_t K, const float *W, const float *b,
+                         int32_t pool_kernel, float *Wp, float *bp);
+
 /* ---- tuning and introspection (not needed for ordinary use) ------------- */
 
 enum {
     /* Split-K control: 0 = automatic (default), 1 = never split, S >= 2 =
      * split K into S slices whose partial sums are added in slice order by
-     * a second pass (deterministic).  Split-K applies to kinds 0, 1 and 3. */
+     * a second pass (deterministic) that also applies the tail (for the
+     * row-max kinds: bias, pooling, GELU, scale and the max). */
     LIN_EPI_OPT_SPLIT_K = 1,
     /* 1 = time every kernel this handle launches with HIP events on its
      * stream (read with lin_epi_profile_read); 0 = off (default). */
-    LIN_EPI_OPT_PROFILE = 2
+    LIN_EPI_OPT_PROFILE = 2,
+    /* 1 = unfused ablation: the GEMM writes the raw linear output (to Y for
+     * kinds 0, 1, 3, to the workspace for kinds 2, 4) and a separate kernel
+     * then applies the tail, as the pages' own solutions do after a library
+     * GEMM; 0 = fused (default).  Same results within the tolerance; exists
+     * to measure what fusion saves. */
+    LIN_EPI_OPT_UNFUSED = 3
 };
 
 int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value);
@@ -114,18 +144,27 @@ typedef struct {
     int32_t tile_m, tile_n, tile_k; /* workgroup output tile and K step */
     int32_t split_k;                /* K slices (1 = no split) */
     int64_t grid_main;              /* workgroups of the GEMM kernel */
-    int32_t kernels;                /* kernels launched (GEMM + reduce/finalize) */
+    int32_t kernels;                /* kernels launched (GEMM + reduce/finalize/tail) */
     int64_t workspace_bytes;        /* workspace the run used */
 } lin_epi_plan;
 
 int lin_epi_last_plan(lin_epi_handle h, lin_epi_plan *out);
 
+/* The plan lin_epi_run would use for this problem, honouring the handle's
+ * options, on a device with `num_cus` compute units (0 = the current
+ * device's count, which needs a HIP call; any positive value makes this a
+ * pure host computation).  M == 0 or N == 0 gives an all-zero plan.  Same
+ * argument checks as lin_epi_run except the pointer ones. */
+int lin_epi_query_plan(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const lin_epi_desc *desc,
+                       int32_t num_cus, lin_epi_plan *out);
+
 /* Accumulated kernel timings since the last read (profiling on).  Waits for
  * the handle's stream.  Role 0 is the GEMM kernel, role 1 the second pass
- * (split-K reduce or row-max finalize). */
+ * (split-K reduce or row-max finalize), role 2 the separate tail kernel of
+ * the unfused ablation and lin_epi_pool_weights. */
 typedef struct {
-    int64_t launches[2];
-    double total_ms[2];
+    int64_t launches[3];
+    double total_ms[3];
 } lin_epi_profile;
 
 int lin_epi_profile_read(lin_epi_handle h, lin_epi_profile *out);

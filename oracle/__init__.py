@@ -175,6 +175,7 @@ KIND_NONE = 0
 KIND_SCALE_HARDTANH_GELU = 1
 KIND_POOL_GELU_SCALE_ROWMAX = 2
 KIND_SWISH_SCALE = 3
+KIND_GELU_SCALE_ROWMAX = 4
 
 
 def apply_tail(y, kind: int, scale: float = 1.0, lo: float = -1.0, hi: float = 1.0, pool_kernel: int = 16):
@@ -187,6 +188,9 @@ def apply_tail(y, kind: int, scale: float = 1.0, lo: float = -1.0, hi: float = 1
         return tail_pool_gelu_scale_rowmax(y, pool_kernel, scale)[0]
     if kind == KIND_SWISH_SCALE:
         return tail_swish_scale(y, scale)
+    if kind == KIND_GELU_SCALE_ROWMAX:
+        # tail (b) with a window of one column: the row max of scale*GELU(y)
+        return tail_pool_gelu_scale_rowmax(y, 1, scale)[0]
     raise ValueError("unknown tail kind %r" % kind)
 
 

@@ -67,6 +67,7 @@ DESC_A = lib.make_desc(lib.LIN_EPI_SCALE_HARDTANH_GELU, 0.5, -2.0, 2.0)
     (dict(K=-4), lib.LIN_EPI_EINVAL),
     (dict(M=2**31), lib.LIN_EPI_EINVAL),
     (dict(desc=lib.make_desc(7)), lib.LIN_EPI_EINVAL),
+    (dict(desc=lib.make_desc(5)), lib.LIN_EPI_EINVAL),
     (dict(desc=lib.make_desc(-1)), lib.LIN_EPI_EINVAL),
     (dict(desc=lib.make_desc(1, 0.5, 2.0, -2.0)), lib.LIN_EPI_EINVAL),
     (dict(desc=lib.make_desc(2, 2.0, pool_kernel=8)), lib.LIN_EPI_ENOTSUP),
@@ -98,12 +99,40 @@ def test_options_and_introspection_validation(handle):
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 65) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 3) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_PROFILE, 2) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 2) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 1) == lib.LIN_EPI_OK
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 0) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, 99, 0) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(0, lib.LIN_EPI_OPT_PROFILE, 1) == lib.LIN_EPI_EINVAL
     rc, _ = lib.lin_epi_last_plan(handle)
     assert rc == lib.LIN_EPI_EINVAL  # nothing has run yet
     rc, prof = lib.lin_epi_profile_read(handle)
-    assert rc == lib.LIN_EPI_OK and prof.launches[0] == 0 and prof.launches[1] == 0
+    assert rc == lib.LIN_EPI_OK and list(prof.launches) == [0, 0, 0]
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(h=None), lib.LIN_EPI_EINVAL),
+    (dict(N=-1), lib.LIN_EPI_EINVAL),
+    (dict(K=-4), lib.LIN_EPI_EINVAL),
+    (dict(pool=0), lib.LIN_EPI_EINVAL),
+    (dict(pool=-16), lib.LIN_EPI_EINVAL),
+    (dict(b=0), lib.LIN_EPI_EINVAL),
+    (dict(bp=0), lib.LIN_EPI_EINVAL),
+    (dict(W=0), lib.LIN_EPI_EINVAL),
+    (dict(Wp=0), lib.LIN_EPI_EINVAL),
+    (dict(K=6), lib.LIN_EPI_EALIGN),
+    (dict(W=A16 + 4), lib.LIN_EPI_EALIGN),
+    (dict(Wp=A16 + 8), lib.LIN_EPI_EALIGN),
+    (dict(bp=A16 + 2), lib.LIN_EPI_EALIGN),
+    # fewer rows than one window: nothing to compute
+    (dict(N=15), lib.LIN_EPI_OK),
+    (dict(N=0, W=0, b=0, Wp=0, bp=0), lib.LIN_EPI_OK),
+])
+def test_pool_weights_validation(handle, args, expect):
+    a = dict(h=handle, N=64, K=16, W=A16, b=A16, pool=16, Wp=A16, bp=A16)
+    a.update(args)
+    rc = lib.lin_epi_pool_weights(a["h"], a["N"], a["K"], a["W"], a["b"], a["pool"], a["Wp"], a["bp"])
+    assert rc == expect, lib.lin_epi_status_string(rc)
 
 
 def test_destroy_null_is_noop():
@@ -113,4 +142,69 @@ def test_destroy_null_is_noop():
 def test_desc_layout_matches_header():
     assert ctypes.sizeof(lib.lin_epi_desc) == 24
     assert ctypes.sizeof(lib.lin_epi_plan) == 40
-    assert ctypes.sizeof(lib.lin_epi_profile) == 32
+    assert ctypes.sizeof(lib.lin_epi_profile) == 48
+
+
+# ---- the planner, evaluated on the host for a 256-CU device ---------------
+
+def _plan(handle, M, N, K, kind, cus=256):
+    rc, p = lib.lin_epi_query_plan(handle, M, N, K, lib.make_desc(kind, 1.0), cus)
+    assert rc == lib.LIN_EPI_OK, lib.lin_epi_status_string(rc)
+    return (p.tile_m, p.tile_n, p.split_k, p.kernels, p.grid_main, p.workspace_bytes)
+
+
+def test_planner_choices_for_the_workloads(handle):
+    A, B, C, F = (lib.LIN_EPI_SCALE_HARDTANH_GELU, lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX, lib.LIN_EPI_SWISH_SCALE,
+                  lib.LIN_EPI_GELU_SCALE_ROWMAX)
+    # 2048x8192x8192: 256x256 tiles, one per compute unit, no split
+    assert _plan(handle, 2048, 8192, 8192, A) == (256, 256, 1, 1, 256, 0)
+    # 128x32768x32768: 128x256 tiles (128 of them) split in two
+    assert _plan(handle, 128, 32768, 32768, C)[:4] == (128, 256, 2, 2)
+    # ragged: 8x24 tiles of 128x256, four K slices -> 768 workgroups = 3 rounds
+    assert _plan(handle, 1000, 6000, 4100, A)[:5] == (128, 256, 4, 2, 768)
+    # pooled-weight tail (b): a 1024x512x8192 GEMM needs 16 slices to fill the device
+    assert _plan(handle, 1024, 512, 8192, F)[:4] == (128, 256, 16, 2)
+    # tail (b) unsplit keeps per-tile row maxima: M * tiles_n floats
+    t = _plan(handle, 1024, 8192, 8192, B)
+    if t[2] == 1:
+        assert t[5] == 1024 * (8192 // t[1]) * 4
+    else:
+        assert t[5] == t[2] * 1024 * 8192 * 4
+
+
+def test_planner_respects_options(handle):
+    A = lib.LIN_EPI_SCALE_HARDTANH_GELU
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 1) == 0
+    assert _plan(handle, 1000, 6000, 4100, A)[2] == 1
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 5) == 0
+    assert _plan(handle, 1000, 6000, 4100, A)[2] == 5
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 0) == 0
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 1) == 0
+    # unfused, no split: GEMM + separate tail kernel; kind 0 has no tail kernel
+    assert _plan(handle, 2048, 8192, 8192, A)[3] == 2
+    assert _plan(handle, 2048, 8192, 8192, lib.LIN_EPI_NONE)[3] == 1
+    # unfused row-max kinds keep the raw output in the workspace
+    assert _plan(handle, 2048, 8192, 8192, lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX)[5] >= 2048 * 8192 * 4
+
+
+def test_planner_every_slice_gets_k(handle):
+    """For any split the last slice still owns K steps: grid_main = tiles * S and
+    S <= ceil(K / 32)."""
+    for K in (4, 32, 36, 100, 1000, 4100):
+        for S in (2, 3, 5, 16):
+            assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, S) == 0
+            tm, tn, s, _, grid, _ = _plan(handle, 300, 300, K, lib.LIN_EPI_NONE)
+            assert 1 <= s <= max(1, -(-K // 32))
+            assert grid == -(-300 // tm) * -(-300 // tn) * s
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 0) == 0
+
+
+def test_query_plan_validation(handle):
+    d = lib.make_desc(lib.LIN_EPI_NONE)
+    assert lib.lin_epi_query_plan(0, 8, 8, 8, d, 256)[0] == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_query_plan(handle, 8, 8, 8, None, 256)[0] == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_query_plan(handle, 8, 8, 8, d, -1)[0] == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_query_plan(handle, 8, 8, 6, d, 256)[0] == lib.LIN_EPI_EALIGN
+    assert lib.lin_epi_query_plan(handle, 8, 8, 8, lib.make_desc(2, pool_kernel=4), 256)[0] == lib.LIN_EPI_ENOTSUP
+    rc, p = lib.lin_epi_query_plan(handle, 0, 8, 8, d, 256)
+    assert rc == 0 and p.grid_main == 0

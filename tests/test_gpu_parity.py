@@ -28,7 +28,7 @@ def _name(request):
     log("== %s" % request.node.nodeid)
 
 
-ALL_TAILS = (workloads.TAIL_A, workloads.TAIL_B, workloads.TAIL_C, workloads.TAIL_NONE)
+ALL_TAILS = (workloads.TAIL_A, workloads.TAIL_B, workloads.TAIL_C, workloads.TAIL_NONE, workloads.TAIL_B_FOLDED)
 
 
 # ---------------------------------------------------------------- small shapes
@@ -134,7 +134,8 @@ def test_tail_a_clipping_exercised(h):
 # ------------------------------------------------------------------ split-K
 
 @pytest.mark.parametrize("S", [2, 3, 5])
-@pytest.mark.parametrize("tail", [workloads.TAIL_A, workloads.TAIL_C, workloads.TAIL_NONE], ids=lambda t: t.name)
+@pytest.mark.parametrize("tail", [workloads.TAIL_A, workloads.TAIL_C, workloads.TAIL_NONE, workloads.TAIL_B,
+                                  workloads.TAIL_B_FOLDED], ids=lambda t: t.name)
 def test_forced_split_k(tail, S):
     M, N, K = 200, 390, 1000
     X, W, b = workloads.make_inputs(M, N, K, seed=31)
@@ -176,7 +177,7 @@ def test_output_guard_bands_untouched(h, tail):
     M, N, K = 131, 200, 36
     X, W, b = workloads.make_inputs(M, N, K, seed=51)
     Xd, Wd, bd = to_dev(X, W, b)
-    n_out = M if tail.kind == workloads.POOL_GELU_SCALE_ROWMAX else M * N
+    n_out = int(np.prod(lib.LinEpi.output_shape(M, N, tail.kind)))
     pad = 4096
     buf = torch.full((n_out + 2 * pad,), float("nan"), dtype=torch.float32, device="cuda:0")
     Y = buf[pad: pad + n_out]
@@ -222,3 +223,24 @@ def test_full_size_workload_checked_rows(h, name):
     log("oracle on %d rows" % rows.size)
     ref = oracle_rows(X, W, b, tail, rows)
     compare(got[rows], ref, what="%s %s (64 rows)" % (name, tail.name))
+
+
+@pytest.mark.parametrize("tail", [workloads.TAIL_A, workloads.TAIL_C, workloads.TAIL_B], ids=lambda t: t.name)
+def test_split_k_output_offset_by_one_float(tail):
+    """Y starting 4 bytes past a 16-byte boundary: the split-K second pass must
+    fall back from 128-bit stores and still write exactly Y."""
+    M, N, K = 70, 264, 1000
+    X, W, b = workloads.make_inputs(M, N, K, seed=91)
+    Xd, Wd, bd = to_dev(X, W, b)
+    n_out = int(np.prod(lib.LinEpi.output_shape(M, N, tail.kind)))
+    buf = torch.full((n_out + 8,), float("nan"), dtype=torch.float32, device="cuda:0")
+    Y = buf[1: 1 + n_out]
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, 3)
+        h.run_into(Xd, Wd, bd, desc_for(tail), Y)
+        torch.cuda.synchronize()
+        assert h.plan().split_k == 3
+    host = buf.cpu().numpy()
+    assert np.isnan(host[0]) and np.isnan(host[1 + n_out:]).all()
+    ref = oracle_rows(X, W, b, tail)
+    compare(host[1: 1 + n_out].reshape(ref.shape), ref, what="offset Y split-3 %s" % tail.name)

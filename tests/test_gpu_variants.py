@@ -1,0 +1,130 @@
+"""GPU parity of the follow-up variants against the CPU oracle:
+
+* the unfused ablation (LIN_EPI_OPT_UNFUSED): GEMM to memory, then a separate
+  tail kernel — must give the same results as the definition;
+* the pooled-weight form of tail (b) (lin_epi_pool_weights + kind 4), the
+  identity page "Kimi-K2.6 l2_p98" derives and checks on a small example.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import dense_linear_layer_amd as lib
+import oracle
+import workloads
+from parity_util import compare, log, oracle_rows, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+ALL_TAILS = (workloads.TAIL_A, workloads.TAIL_B, workloads.TAIL_C, workloads.TAIL_NONE, workloads.TAIL_B_FOLDED)
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    log("== %s" % request.node.nodeid)
+
+
+# ---------------------------------------------------------------- unfused
+
+@pytest.mark.parametrize("M,N,K", [(5, 48, 12), (130, 290, 100), (257, 1040, 520), (64, 16, 8)])
+@pytest.mark.parametrize("tail", ALL_TAILS, ids=lambda t: t.name)
+def test_unfused_matches_oracle(M, N, K, tail):
+    X, W, b = workloads.make_inputs(M, N, K, seed=7 * M + N)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_UNFUSED, 1)
+        got = run_gpu(h, *to_dev(X, W, b), tail)
+        p = h.plan()
+        assert p.kernels == (2 if p.split_k > 1 else 1) + (0 if tail.kind == workloads.NONE else 1)
+    compare(got, oracle_rows(X, W, b, tail), what="unfused %dx%dx%d %s" % (M, N, K, tail.name))
+
+
+@pytest.mark.parametrize("tail", ALL_TAILS, ids=lambda t: t.name)
+def test_unfused_with_split_k(tail):
+    X, W, b = workloads.make_inputs(200, 390, 1000, seed=71)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_UNFUSED, 1)
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, 3)
+        got = run_gpu(h, *to_dev(X, W, b), tail)
+        assert h.plan().split_k == 3
+    compare(got, oracle_rows(X, W, b, tail), what="unfused split-3 %s" % tail.name)
+
+
+def test_unfused_equals_fused_on_integer_inputs():
+    """Integer inputs make the GEMM exact, so the raw outputs of both paths are
+    identical and the tails see the same arguments."""
+    X, W, b = workloads.integer_inputs(300, 520, 260, seed=72)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        fused = run_gpu(h, Xd, Wd, bd, workloads.TAIL_NONE)
+        h.set_option(lib.LIN_EPI_OPT_UNFUSED, 1)
+        unfused = run_gpu(h, Xd, Wd, bd, workloads.TAIL_NONE)
+    assert np.array_equal(fused, unfused)
+
+
+# ------------------------------------------------------ pooled weights (f1)
+
+def test_pool_weights_match_oracle_pooling():
+    N, K = 16 * 37 + 5, 260
+    _, W, b = workloads.make_inputs(1, N, K, seed=81)
+    Wd, bd = to_dev(W, b)
+    with lib.LinEpi() as h:
+        Wp, bp = h.pool_weights(Wd, bd, 16)
+        torch.cuda.synchronize()
+    ref_W = oracle.avgpool1d(W.T.astype(np.float64), 16).T
+    ref_b = oracle.avgpool1d(b[None, :].astype(np.float64), 16)[0]
+    assert Wp.shape == (37, K) and bp.shape == (37,)
+    # 16 fp32 additions then an exact scaling by 1/16: a few ulp
+    np.testing.assert_allclose(Wp.cpu().numpy(), ref_W, rtol=0, atol=8 * 2**-24 * np.abs(W).max())
+    np.testing.assert_allclose(bp.cpu().numpy(), ref_b, rtol=0, atol=8 * 2**-24 * np.abs(b).max())
+
+
+def test_pool_weights_worked_example_from_page():
+    """Page l2_p98's hand check: x = [1, 2], W = [[1,0],[0,1],[1,1],[2,2]],
+    b = 0, window 2 gives pooled weights [[0.5,0.5],[1.5,1.5]] and pooled
+    output [1.5, 4.5].  K is padded with zeros to the 4-float row granule."""
+    g = json.load(open(os.path.join(GOLDEN, "pool_fold_worked_example.json")))
+    pad = lambda a: np.pad(np.array(a, dtype=np.float32), ((0, 0), (0, 2)))
+    X, W = pad(g["x"]), pad(g["W"])
+    b = np.array(g["b"], dtype=np.float32)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        Wp, bp = h.pool_weights(Wd, bd, g["pool_kernel"])
+        y = h.run(Xd, Wp, bp, lib.make_desc(lib.LIN_EPI_NONE))
+        torch.cuda.synchronize()
+    assert np.array_equal(Wp.cpu().numpy()[:, :2], np.array(g["pooled_weight"], dtype=np.float32))
+    assert np.array_equal(y.cpu().numpy(), np.array(g["pooled"], dtype=np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 1024, 520), (37, 6000, 4100), (1, 16, 4), (129, 16 * 33 + 7, 64)])
+def test_pool_fold_tail_b_matches_definition(M, N, K):
+    """Tail (b) of the original layer, computed as kind 4 on pooled weights,
+    against the oracle's unfolded definition (pool the linear output)."""
+    X, W, b = workloads.make_inputs(M, N, K, seed=M + 3 * N)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        Wp, bp = h.pool_weights(Wd, bd, 16)
+        got = run_gpu(h, Xd, Wp, bp, workloads.TAIL_B_FOLDED)
+    compare(got, oracle_rows(X, W, b, workloads.TAIL_B), what="pool-fold %dx%dx%d" % (M, N, K))
+
+
+def test_pool_fold_full_size_checked_rows():
+    w = workloads.WORKLOADS["p2_1024x8192x8192"]
+    X, W, b = workloads.make_inputs(w.M, w.N, w.K, seed=w.seed)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        Wp, bp = h.pool_weights(Wd, bd, 16)
+        got = run_gpu(h, Xd, Wp, bp, workloads.TAIL_B_FOLDED)
+        fused = run_gpu(h, Xd, Wd, bd, workloads.TAIL_B)
+    rows = workloads.checked_rows(w.M, seed=w.seed)
+    ref = oracle_rows(X, W, b, workloads.TAIL_B, rows)
+    compare(got[rows], ref, what="pool-fold 1024x8192x8192 (64 rows)")
+    # the folded and the direct form agree to fp32 rounding on every row
+    compare(got, fused, tol=1e-4, what="pool-fold vs fused direct (all rows)")

@@ -29,13 +29,14 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # Tail kinds (the numbering of the C interface's epilogue descriptor).
-NONE, SCALE_HARDTANH_GELU, POOL_GELU_SCALE_ROWMAX, SWISH_SCALE = 0, 1, 2, 3
+NONE, SCALE_HARDTANH_GELU, POOL_GELU_SCALE_ROWMAX, SWISH_SCALE, GELU_SCALE_ROWMAX = 0, 1, 2, 3, 4
 
 TAIL_NAMES = {
     NONE: "linear",
     SCALE_HARDTANH_GELU: "scale_hardtanh_gelu",
     POOL_GELU_SCALE_ROWMAX: "avgpool16_gelu_scale_rowmax",
     SWISH_SCALE: "swish_scale",
+    GELU_SCALE_ROWMAX: "gelu_scale_rowmax",
 }
 
 
@@ -59,6 +60,7 @@ TAIL_A = Tail(SCALE_HARDTANH_GELU, scale=0.5, lo=-2.0, hi=2.0)   # page l2_p53
 TAIL_B = Tail(POOL_GELU_SCALE_ROWMAX, scale=2.0, pool_kernel=16)  # page l2_p98
 TAIL_C = Tail(SWISH_SCALE, scale=2.0)                             # page l2_p59
 TAIL_NONE = Tail(NONE)
+TAIL_B_FOLDED = Tail(GELU_SCALE_ROWMAX, scale=2.0)                # tail (b) on pooled weights
 
 
 @dataclass(frozen=True)
