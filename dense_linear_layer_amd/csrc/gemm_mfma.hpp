@@ -205,29 +205,33 @@ gemm_epi_kernel(GemmArgs a)
     };
 
     // Software pipeline over K steps (one LDS stage = BK of K per step):
-    //   * the next step's tile is fetched into registers at the top of a step
-    //     and written to the other LDS stage before the step's last MFMA
-    //     group is issued, so the stores complete under MFMA work;
+    //   * step kt+1's tile is written to the other LDS stage before step kt's
+    //     second-to-last MFMA group, so the stores complete under MFMA work;
+    //   * the registers it came from receive the global loads of step kt+2
+    //     right after that group's MFMAs are issued (the issue slots before
+    //     the barrier are otherwise idle), so the loads have a whole step to
+    //     arrive;
     //   * the last group's MFMAs are issued after the barrier, together with
     //     the LDS reads of the next step's first group, so the matrix pipe
-    //     has queued work while those reads are in flight.
+    //     has queued work while the barrier and those reads resolve.
     // The other stage is free to overwrite: every wavefront finished reading
     // it before the previous barrier.
     if (nk > 0) {
         gload(kbeg);
         sstore(0);
+        if (nk > 1) gload(kbeg + BK);
         __syncthreads();
         read_frags(0, 0, fa[0], fb[0]);
     }
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
         const int buf = kt & 1;
-        if (more) gload(kbeg + (kt + 1) * BK);
 #pragma unroll
         for (int g = 0; g < G - 1; ++g) {
             read_frags(buf, (g + 1) * 8, fa[(g + 1) & 1], fb[(g + 1) & 1]);
             if (g == G - 2 && more) sstore(buf ^ 1);
             mfma_group(fa[g & 1], fb[g & 1]);
+            if (g == G - 2 && kt + 2 < nk) gload(kbeg + (kt + 2) * BK);
         }
         // Keep the stores and the second-to-last group's MFMAs ahead of the
         // barrier, and the next step's first LDS reads ahead of the last
