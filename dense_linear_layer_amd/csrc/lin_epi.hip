@@ -14,31 +14,44 @@ using namespace lin_epi;
 
 namespace {
 
-// Tile table.  All three use v_mfma_f32_32x32x2_f32, a K step of 32 and a
+// Tile table.  All use v_mfma_f32_32x32x2_f32, a K step of 32 and a
 // double-buffered LDS stage; they differ in workgroup tile and wavefront
 // count, and the dispatcher picks one per call (choose_plan below):
 //   LARGE  256x256, 8 wavefronts (4x2, 64x128 each), 144 KiB LDS, 1 WG/CU
 //   MID    128x256, 8 wavefronts (2x4, 64x64 each),  108 KiB LDS, 1 WG/CU
 //   SMALL  128x128, 4 wavefronts (2x2, 64x64 each),   72 KiB LDS, 2 WG/CU
+//   TINY    64x64,  4 wavefronts (2x2, 32x32 each),   36 KiB LDS, 4 WG/CU
 using CfgLarge = TileCfg<256, 256, 32, 4, 2, 1>;
 using CfgMid = TileCfg<128, 256, 32, 2, 4, 1>;
 using CfgSmall = TileCfg<128, 128, 32, 2, 2, 2>;
+using CfgTiny = TileCfg<64, 64, 32, 2, 2, 4>;
 
-enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_COUNT = 3 };
+enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_COUNT = 4 };
 
 struct CfgInfo {
     int bm, bn, bk, wgs_per_cu;
-    double speed;  // relative MFMA efficiency at full occupancy (measured on MI355X)
+    double efficiency;  // fraction of the CU's 2.4 GHz fp32 MFMA peak, fitted to MI355X timings
 };
 
 constexpr CfgInfo kCfgs[CFG_COUNT] = {
-    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, 1, 1.035},
-    {CfgMid::BM, CfgMid::BN, CfgMid::BK, 1, 1.01},
-    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, 2, 1.0},
+    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, 0.90},
+    {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, 0.86},
+    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, 0.78},
+    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, 0.60},
 };
-static_assert(CfgLarge::LDS_BYTES <= 160 * 1024 && CfgMid::LDS_BYTES <= 160 * 1024 &&
-                  2 * CfgSmall::LDS_BYTES <= 160 * 1024,
+static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
+                  CfgMid::LDS_BYTES * CfgMid::WG_PER_CU <= 160 * 1024 &&
+                  CfgSmall::LDS_BYTES * CfgSmall::WG_PER_CU <= 160 * 1024 &&
+                  CfgTiny::LDS_BYTES * CfgTiny::WG_PER_CU <= 160 * 1024,
               "LDS budget");
+
+// Time-model constants of the planner, fitted (with the efficiencies above)
+// to 70 timed (shape, configuration, split) combinations on MI355X so that
+// the chosen plan is within a few percent of the best one measured.
+constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at the 2.4 GHz peak clock
+constexpr double kRoundFixedS = 4e-6;           // per round of workgroups: first loads, epilogue, drain
+constexpr double kPassFixedS = 3e-6;            // one more kernel on the stream
+constexpr double kPassBytesPerS = 3e12;         // sustained HBM rate of the second passes
 
 struct PendingTiming {
     int role;
@@ -54,6 +67,7 @@ struct lin_epi_ctx {
     void *ws = nullptr;
     size_t ws_bytes = 0;
     int64_t split_opt = 0;
+    int64_t tile_opt = 0;
     bool profile = false;
     bool unfused = false;
     bool has_plan = false;
@@ -126,7 +140,8 @@ void launch_gemm(int cfg, const GemmArgs &g, int64_t grid_x, int split, hipStrea
     switch (cfg) {
         case CFG_LARGE: launch_gemm_cfg<CfgLarge, EPI>(g, grid_x, split, s); break;
         case CFG_MID: launch_gemm_cfg<CfgMid, EPI>(g, grid_x, split, s); break;
-        default: launch_gemm_cfg<CfgSmall, EPI>(g, grid_x, split, s); break;
+        case CFG_SMALL: launch_gemm_cfg<CfgSmall, EPI>(g, grid_x, split, s); break;
+        default: launch_gemm_cfg<CfgTiny, EPI>(g, grid_x, split, s); break;
     }
 }
 
@@ -149,42 +164,49 @@ struct Plan {
     int tiles_m, tiles_n;
 };
 
-// Pick the tile configuration and the number of K slices.  For every
-// candidate the model scores
-//   speed(cfg) * useful(cfg) * balance(cfg, S) / (1 + reduce_cost(S)),
-// where useful is the fraction of computed outputs that lie inside M x N,
-// balance is the fraction of workgroup slots busy over the rounds needed to
-// run tiles*S workgroups on this device, and reduce_cost is the second pass
-// relative to the GEMM: S partial reads plus one output write of M*N floats
-// at ~4 TB/s against 2*M*N*K FLOP at ~120 TFLOP/s, i.e. (S + 1) * 60 / K.
-// A slice keeps at least 8 K steps.  LIN_EPI_OPT_SPLIT_K overrides S.  For
-// the row-max tails a split moves pooling, GELU and the max into the second
-// pass, which reads complete sums.
-Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int num_cus)
+// Pick the tile configuration and the number of K slices by estimated time.
+// For each configuration and slice count S (1..16, at most one per K step):
+//   units = tiles * S workgroups, each computing a BM x BN tile over
+//   ceil(steps / S) K steps; the busiest CU runs load = ceil(units / CUs) of
+//   them, w = WG_PER_CU at a time, sharing its matrix pipes, so
+//     t_gemm = ceil(load / w) * t_round + load * 2*BM*BN*k_slice / (peak * eff)
+//   and a second pass (split-K or row-max finalize) costs
+//     t_pass = t_launch + (S + 1) * M * N * 4 bytes / HBM rate   (S > 1)
+//            = t_launch                                          (S = 1, row max)
+// Padding waste is included (a tile's work counts in full).  The fastest
+// estimate wins; LIN_EPI_OPT_SPLIT_K = 1 forbids a split and S >= 2 forces
+// one (clamped to the K steps available, so every slice owns at least one).
+// For the row-max tails a split moves pooling, GELU and the max into the
+// second pass, which reads complete sums.
+Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind, int num_cus)
 {
     Plan best{CFG_SMALL, 1, 0, 0, 0};
-    double best_score = -1.0;
+    double best_t = 1e300;
+    // (every configuration that is not excluded by the override scores at
+    // least S = 1, so `best` is always set)
+    const bool rowmax = kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX || kind == LIN_EPI_GELU_SCALE_ROWMAX;
     for (int c = 0; c < CFG_COUNT; ++c) {
         const CfgInfo &ci = kCfgs[c];
         const int64_t tm = (M + ci.bm - 1) / ci.bm, tn = (N + ci.bn - 1) / ci.bn;
         const int64_t tiles = tm * tn;
-        const double useful = (double)M * (double)N / ((double)tm * ci.bm * (double)tn * ci.bn);
-        const int64_t slots = (int64_t)num_cus * ci.wgs_per_cu;
         const int64_t steps = (K + ci.bk - 1) / ci.bk;
-        // A forced split is clamped to the K steps available, so every slice
-        // owns at least one; the first candidate (S = s_lo) is always scored.
-        int s_lo = 1, s_hi = 16;
+        if (h->tile_opt > 0 && c != h->tile_opt - 1) continue;
+        int s_lo = 1, s_hi = (int)std::min<int64_t>(16, std::max<int64_t>(steps, 1));
         if (h->split_opt == 1) s_hi = 1;
         if (h->split_opt >= 2) s_lo = s_hi = (int)std::min<int64_t>(h->split_opt, std::max<int64_t>(steps, 1));
         for (int S = s_lo; S <= s_hi; ++S) {
-            if (S > s_lo && steps < 8 * S) break;
             const int64_t units = tiles * S;
-            const int64_t rounds = (units + slots - 1) / slots;
-            const double balance = (double)units / (double)(rounds * slots);
-            const double reduce_cost = S > 1 ? (S + 1) * 60.0 / (double)K : 0.0;
-            const double score = ci.speed * useful * balance / (1.0 + reduce_cost);
-            if (score > best_score) {
-                best_score = score;
+            const int64_t load = (units + num_cus - 1) / num_cus;
+            const int64_t kslice = ((steps + S - 1) / S) * ci.bk;
+            const double wg_flops = 2.0 * ci.bm * ci.bn * (double)kslice;
+            double t = (double)((load + ci.wgs_per_cu - 1) / ci.wgs_per_cu) * kRoundFixedS +
+                       (double)load * wg_flops / (kCuPeakFlops * ci.efficiency);
+            if (S > 1)
+                t += kPassFixedS + (S + 1) * (double)M * (double)N * 4.0 / kPassBytesPerS;
+            else if (rowmax)
+                t += kPassFixedS;
+            if (t < best_t) {
+                best_t = t;
                 best = Plan{c, S, 0, (int)tm, (int)tn};
             }
         }
@@ -315,6 +337,10 @@ int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value)
             if (value != 0 && value != 1) return LIN_EPI_EINVAL;
             h->profile = value != 0;
             return LIN_EPI_OK;
+        case LIN_EPI_OPT_TILE:
+            if (value < 0 || value > CFG_COUNT) return LIN_EPI_EINVAL;
+            h->tile_opt = value;
+            return LIN_EPI_OK;
         case LIN_EPI_OPT_UNFUSED:
             if (value != 0 && value != 1) return LIN_EPI_EINVAL;
             h->unfused = value != 0;
@@ -375,7 +401,7 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
 
     const bool rowmax = is_rowmax(kind);
     const bool unfused = h->unfused;
-    const Plan pl = choose_plan(h, M, N, K, h->num_cus);
+    const Plan pl = choose_plan(h, M, N, K, kind, h->num_cus);
     const int tiles_m = pl.tiles_m, tiles_n = pl.tiles_n;
     const int64_t tiles = (int64_t)tiles_m * tiles_n;
     const int split = pl.split;
@@ -530,7 +556,7 @@ int lin_epi_query_plan(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const 
     }
     *out = lin_epi_plan{};
     if (M == 0 || N == 0) return LIN_EPI_OK;
-    const Plan pl = choose_plan(h, M, N, K, num_cus);
+    const Plan pl = choose_plan(h, M, N, K, desc->kind, num_cus);
     *out = describe(h, pl, M, N, desc->kind);
     return LIN_EPI_OK;
 }

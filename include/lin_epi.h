@@ -134,7 +134,11 @@ enum {
      * then applies the tail, as the pages' own solutions do after a library
      * GEMM; 0 = fused (default).  Same results within the tolerance; exists
      * to measure what fusion saves. */
-    LIN_EPI_OPT_UNFUSED = 3
+    LIN_EPI_OPT_UNFUSED = 3,
+    /* Tile configuration: 0 = automatic (default); 1 = 256x256 tiles with 8
+     * wavefronts, 2 = 128x256 with 8, 3 = 128x128 with 4, 4 = 64x64 with 4.
+     * The split-K choice is still made (or forced) as usual. */
+    LIN_EPI_OPT_TILE = 4
 };
 
 int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value);

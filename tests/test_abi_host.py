@@ -102,6 +102,10 @@ def test_options_and_introspection_validation(handle):
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 2) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 1) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 0) == lib.LIN_EPI_OK
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 5) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, -1) == lib.LIN_EPI_EINVAL
+    for t in range(5):
+        assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, t) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, 99, 0) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(0, lib.LIN_EPI_OPT_PROFILE, 1) == lib.LIN_EPI_EINVAL
     rc, _ = lib.lin_epi_last_plan(handle)
@@ -185,6 +189,20 @@ def test_planner_respects_options(handle):
     assert _plan(handle, 2048, 8192, 8192, lib.LIN_EPI_NONE)[3] == 1
     # unfused row-max kinds keep the raw output in the workspace
     assert _plan(handle, 2048, 8192, 8192, lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX)[5] >= 2048 * 8192 * 4
+
+
+def test_planner_tile_override(handle):
+    for t, shape in lib.TILE_CONFIGS.items():
+        assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, t) == 0
+        assert _plan(handle, 2048, 8192, 8192, lib.LIN_EPI_NONE)[:2] == shape
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 0) == 0
+
+
+def test_planner_small_problems_spread_out(handle):
+    # 64x256x256 would be one 128x256 workgroup; the planner spreads it over
+    # 64x64 tiles and K slices instead
+    tm, tn, s, k, grid, _ = _plan(handle, 64, 256, 256, lib.LIN_EPI_SCALE_HARDTANH_GELU)
+    assert (tm, tn) == (64, 64) and grid >= 16
 
 
 def test_planner_every_slice_gets_k(handle):

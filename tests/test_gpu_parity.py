@@ -244,3 +244,33 @@ def test_split_k_output_offset_by_one_float(tail):
     assert np.isnan(host[0]) and np.isnan(host[1 + n_out:]).all()
     ref = oracle_rows(X, W, b, tail)
     compare(host[1: 1 + n_out].reshape(ref.shape), ref, what="offset Y split-3 %s" % tail.name)
+
+
+# ------------------------------------------------- every tile configuration
+
+@pytest.mark.parametrize("split", [1, 3])
+@pytest.mark.parametrize("tile", sorted(lib.TILE_CONFIGS))
+@pytest.mark.parametrize("M,N,K", [(37, 200, 68), (300, 17, 1028), (257, 513, 100), (1, 1, 4)])
+def test_every_tile_config_integer_exact(tile, split, M, N, K):
+    """The planner may pick any configuration; each one must be bit-exact on
+    integer inputs, with and without split-K, on shapes ragged in M, N, K."""
+    X, W, b = workloads.integer_inputs(M, N, K, seed=M * N + K)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_TILE, tile)
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, split)
+        got = run_gpu(h, *to_dev(X, W, b), workloads.TAIL_NONE)
+        p = h.plan()
+        assert (p.tile_m, p.tile_n) == lib.TILE_CONFIGS[tile]
+    assert np.array_equal(got.astype(np.float64), oracle.linear_rows(X, W, b))
+
+
+@pytest.mark.parametrize("tile", sorted(lib.TILE_CONFIGS))
+@pytest.mark.parametrize("tail", ALL_TAILS, ids=lambda t: t.name)
+def test_every_tile_config_all_tails(tile, tail):
+    M, N, K = 130, 290, 100
+    X, W, b = workloads.make_inputs(M, N, K, seed=tile)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_TILE, tile)
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, 1)
+        got = run_gpu(h, *to_dev(X, W, b), tail)
+    compare(got, oracle_rows(X, W, b, tail), what="tile %d %s" % (tile, tail.name))
