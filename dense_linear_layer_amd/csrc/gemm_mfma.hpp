@@ -106,11 +106,12 @@ gemm_epi_kernel(GemmArgs a)
     constexpr int TN = BN / WAVES_N;
     constexpr int FM = TM / 32;             // 32x32 MFMA blocks per wave
     constexpr int FN = TN / 32;
-    constexpr int C4 = BK / 4;              // float4 per tile row
-    constexpr int A_LD = BM * C4 / NT;      // float4 global loads per thread
-    constexpr int B_LD = BN * C4 / NT;
+    constexpr int C4 = BK / 4;                    // float4 per tile row
+    constexpr int A_LD = (BM * C4 + NT - 1) / NT;  // float4 global loads per thread
+    constexpr int B_LD = (BN * C4 + NT - 1) / NT;
+    constexpr bool A_EVEN = A_LD * NT == BM * C4;  // else the last round is partial
+    constexpr bool B_EVEN = B_LD * NT == BN * C4;
     static_assert(BK % 8 == 0 && TM % 32 == 0 && TN % 32 == 0, "tile shape");
-    static_assert((BM * C4) % NT == 0 && (BN * C4) % NT == 0, "load split");
 
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
@@ -140,7 +141,8 @@ gemm_epi_kernel(GemmArgs a)
             const int gk = k0 + (idx % C4) * 4;
             const int gm = m0 + row;
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (gm < M && gk < kend) v = *reinterpret_cast<const f32x4 *>(a.X + (int64_t)gm * K + gk);
+            if ((A_EVEN || idx < BM * C4) && gm < M && gk < kend)
+                v = *reinterpret_cast<const f32x4 *>(a.X + (int64_t)gm * K + gk);
             ra[i] = v;
         }
 #pragma unroll
@@ -150,7 +152,8 @@ gemm_epi_kernel(GemmArgs a)
             const int gk = k0 + (idx % C4) * 4;
             const int gn = n0 + row;
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (gn < N && gk < kend) v = *reinterpret_cast<const f32x4 *>(a.W + (int64_t)gn * K + gk);
+            if ((B_EVEN || idx < BN * C4) && gn < N && gk < kend)
+                v = *reinterpret_cast<const f32x4 *>(a.W + (int64_t)gn * K + gk);
             rb[i] = v;
         }
     };
@@ -160,12 +163,12 @@ gemm_epi_kernel(GemmArgs a)
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
             const int idx = tid + i * NT;
-            *reinterpret_cast<f32x4 *>(As + (idx / C4) * LDK + (idx % C4) * 4) = ra[i];
+            if (A_EVEN || idx < BM * C4) *reinterpret_cast<f32x4 *>(As + (idx / C4) * LDK + (idx % C4) * 4) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) {
             const int idx = tid + i * NT;
-            *reinterpret_cast<f32x4 *>(Bs + (idx / C4) * LDK + (idx % C4) * 4) = rb[i];
+            if (B_EVEN || idx < BN * C4) *reinterpret_cast<f32x4 *>(Bs + (idx / C4) * LDK + (idx % C4) * 4) = rb[i];
         }
     };
 

@@ -15,18 +15,23 @@ using namespace lin_epi;
 namespace {
 
 // Tile table.  All use v_mfma_f32_32x32x2_f32, a K step of 32 and a
-// double-buffered LDS stage; they differ in workgroup tile and wavefront
+// double-buffered LDS stage (the skinny one a K step of 64, to keep more
+// weight bytes in flight); they differ in workgroup tile and wavefront
 // count, and the dispatcher picks one per call (choose_plan below):
 //   LARGE  256x256, 8 wavefronts (4x2, 64x128 each), 144 KiB LDS, 1 WG/CU
 //   MID    128x256, 8 wavefronts (2x4, 64x64 each),  108 KiB LDS, 1 WG/CU
 //   SMALL  128x128, 4 wavefronts (2x2, 64x64 each),   72 KiB LDS, 2 WG/CU
 //   TINY    64x64,  4 wavefronts (2x2, 32x32 each),   36 KiB LDS, 4 WG/CU
+//   SKINNY  32x256, 8 wavefronts (1x8, 32x32 each),  153 KiB LDS, 1 WG/CU:
+//           few rows of X against a long stream of W rows (the small-M,
+//           weight-streaming regime, where HBM rather than MFMA bounds)
 using CfgLarge = TileCfg<256, 256, 32, 4, 2, 1>;
 using CfgMid = TileCfg<128, 256, 32, 2, 4, 1>;
 using CfgSmall = TileCfg<128, 128, 32, 2, 2, 2>;
 using CfgTiny = TileCfg<64, 64, 32, 2, 2, 4>;
+using CfgSkinny = TileCfg<32, 256, 64, 1, 8, 1>;
 
-enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_COUNT = 4 };
+enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_COUNT = 5 };
 
 struct CfgInfo {
     int bm, bn, bk, wgs_per_cu;
@@ -38,11 +43,13 @@ constexpr CfgInfo kCfgs[CFG_COUNT] = {
     {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, 0.86},
     {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, 0.78},
     {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, 0.60},
+    {CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, CfgSkinny::WG_PER_CU, 0.60},
 };
 static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
                   CfgMid::LDS_BYTES * CfgMid::WG_PER_CU <= 160 * 1024 &&
                   CfgSmall::LDS_BYTES * CfgSmall::WG_PER_CU <= 160 * 1024 &&
-                  CfgTiny::LDS_BYTES * CfgTiny::WG_PER_CU <= 160 * 1024,
+                  CfgTiny::LDS_BYTES * CfgTiny::WG_PER_CU <= 160 * 1024 &&
+                  CfgSkinny::LDS_BYTES * CfgSkinny::WG_PER_CU <= 160 * 1024,
               "LDS budget");
 
 // Time-model constants of the planner, fitted (with the efficiencies above)
@@ -52,6 +59,7 @@ constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at
 constexpr double kRoundFixedS = 4e-6;           // per round of workgroups: first loads, epilogue, drain
 constexpr double kPassFixedS = 3e-6;            // one more kernel on the stream
 constexpr double kPassBytesPerS = 3e12;         // sustained HBM rate of the second passes
+constexpr double kGemmBytesPerS = 5.6e12;       // sustained HBM rate of a weight-streaming GEMM
 
 struct PendingTiming {
     int role;
@@ -141,7 +149,8 @@ void launch_gemm(int cfg, const GemmArgs &g, int64_t grid_x, int split, hipStrea
         case CFG_LARGE: launch_gemm_cfg<CfgLarge, EPI>(g, grid_x, split, s); break;
         case CFG_MID: launch_gemm_cfg<CfgMid, EPI>(g, grid_x, split, s); break;
         case CFG_SMALL: launch_gemm_cfg<CfgSmall, EPI>(g, grid_x, split, s); break;
-        default: launch_gemm_cfg<CfgTiny, EPI>(g, grid_x, split, s); break;
+        case CFG_TINY: launch_gemm_cfg<CfgTiny, EPI>(g, grid_x, split, s); break;
+        default: launch_gemm_cfg<CfgSkinny, EPI>(g, grid_x, split, s); break;
     }
 }
 
@@ -170,7 +179,8 @@ struct Plan {
 //   ceil(steps / S) K steps; the busiest CU runs load = ceil(units / CUs) of
 //   them, w = WG_PER_CU at a time, sharing its matrix pipes, so
 //     t_gemm = ceil(load / w) * t_round + load * 2*BM*BN*k_slice / (peak * eff)
-//   and a second pass (split-K or row-max finalize) costs
+//   (but never less than the time to stream W and X from HBM once), and a
+//   second pass (split-K or row-max finalize) costs
 //     t_pass = t_launch + (S + 1) * M * N * 4 bytes / HBM rate   (S > 1)
 //            = t_launch                                          (S = 1, row max)
 // Padding waste is included (a tile's work counts in full).  The fastest
@@ -201,6 +211,8 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
             const double wg_flops = 2.0 * ci.bm * ci.bn * (double)kslice;
             double t = (double)((load + ci.wgs_per_cu - 1) / ci.wgs_per_cu) * kRoundFixedS +
                        (double)load * wg_flops / (kCuPeakFlops * ci.efficiency);
+            // every byte of W (and of X) crosses HBM at least once
+            t = std::max(t, 4.0 * ((double)N * K + (double)M * K) / kGemmBytesPerS);
             if (S > 1)
                 t += kPassFixedS + (S + 1) * (double)M * (double)N * 4.0 / kPassBytesPerS;
             else if (rowmax)

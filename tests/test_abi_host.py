@@ -102,9 +102,9 @@ def test_options_and_introspection_validation(handle):
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 2) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 1) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 0) == lib.LIN_EPI_OK
-    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 5) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 6) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, -1) == lib.LIN_EPI_EINVAL
-    for t in range(5):
+    for t in range(6):
         assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, t) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, 99, 0) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(0, lib.LIN_EPI_OPT_PROFILE, 1) == lib.LIN_EPI_EINVAL

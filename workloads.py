@@ -71,10 +71,16 @@ class Workload:
     K: int
     tails: tuple = field(default_factory=tuple)
     seed: int = 0
+    bound: str = "mfma"  # the roofline that bounds it: "mfma" or "hbm"
 
     @property
     def flops(self) -> int:
         return 2 * self.M * self.N * self.K
+
+    def algorithmic_bytes(self, tail: Tail) -> int:
+        """Compulsory HBM bytes of one call: X, W, b read once, Y written once."""
+        out = self.M if tail.kind in (POOL_GELU_SCALE_ROWMAX, GELU_SCALE_ROWMAX) else self.M * self.N
+        return 4 * (self.M * self.K + self.N * self.K + self.N + out)
 
 
 WORKLOADS = {
@@ -83,6 +89,9 @@ WORKLOADS = {
     "p2_1024x8192x8192": Workload("p2_1024x8192x8192", 1024, 8192, 8192, (TAIL_B,)),
     "p3_128x32768x32768": Workload("p3_128x32768x32768", 128, 32768, 32768, (TAIL_C,)),
     "ragged_1000x6000x4100": Workload("ragged_1000x6000x4100", 1000, 6000, 4100, (TAIL_A, TAIL_B, TAIL_C)),
+    # page l2_p59's layer with a decode-size batch: 16 rows against a 4 GiB
+    # weight, bounded by streaming W from HBM rather than by the matrix cores
+    "p3_m16_16x32768x32768": Workload("p3_m16_16x32768x32768", 16, 32768, 32768, (TAIL_C,), bound="hbm"),
 }
 
 
