@@ -102,6 +102,8 @@ def main() -> int:
                     help="time the unfused ablation (GEMM to memory, then a separate tail kernel)")
     ap.add_argument("--pool-fold", action="store_true",
                     help="tail (b) via window-averaged weights: the GEMM is M x N/16 x K (FLOPs counted as such)")
+    ap.add_argument("--scale-fold", action="store_true",
+                    help="tail (a) with its scale folded into W and b (scale 1 in the epilogue)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -151,6 +153,19 @@ def main() -> int:
         prep_ms = e0.elapsed_time(e1)
         tail = workloads.TAIL_B_FOLDED
         flops = 2.0 * w.M * (w.N // 16) * w.K
+    elif args.scale_fold:
+        if tail.kind != workloads.SCALE_HARDTANH_GELU:
+            print("--scale-fold applies to tail (a) only (the other tails scale after a nonlinearity)",
+                  file=sys.stderr)
+            return 2
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            e0.record(stream)
+            Wd_run, bd_run = h.scale_weights(Wd, bd, tail.scale)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        prep_ms = e0.elapsed_time(e1)
+        tail = workloads.Tail(tail.kind, scale=1.0, lo=tail.lo, hi=tail.hi)
     else:
         Wd_run, bd_run = Wd, bd
     desc = lib.make_desc(tail.kind, tail.scale, tail.lo, tail.hi, tail.pool_kernel)
@@ -232,11 +247,14 @@ def main() -> int:
             "split_k": plan.split_k,
             "kernels_per_step": plan.kernels,
             "frac_of_fp32_mfma_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
-            "variant": "pool_fold" if args.pool_fold else ("unfused" if args.unfused else "fused"),
+            "variant": ("pool_fold" if args.pool_fold else "scale_fold" if args.scale_fold
+                        else "unfused" if args.unfused else "fused"),
         },
         "roofline": roofline,
         "parity_spot_check": {"rows": 4, "max_abs_err": spot_err, "ok": spot_ok},
     }
+    if args.scale_fold:
+        out["config"]["scale_weights_prep_ms"] = round(prep_ms, 5)
     if args.pool_fold:
         out["config"]["pool_weights_prep_ms"] = round(prep_ms, 5)
         out["config"]["gemm_flops_counted"] = "2*M*(N/16)*K"

@@ -44,6 +44,7 @@ EXPORTS = (
     "lin_epi_destroy",
     "lin_epi_status_string",
     "lin_epi_pool_weights",
+    "lin_epi_scale_weights",
     "lin_epi_set_option",
     "lin_epi_last_plan",
     "lin_epi_query_plan",
@@ -109,6 +110,8 @@ def load_library():
     lib.lin_epi_status_string.restype = ctypes.c_char_p
     lib.lin_epi_pool_weights.argtypes = [p, i64, i64, p, p, i32, p, p]
     lib.lin_epi_pool_weights.restype = ctypes.c_int
+    lib.lin_epi_scale_weights.argtypes = [p, i64, i64, p, p, ctypes.c_float, p, p]
+    lib.lin_epi_scale_weights.restype = ctypes.c_int
     lib.lin_epi_set_option.argtypes = [p, i32, i64]
     lib.lin_epi_set_option.restype = ctypes.c_int
     lib.lin_epi_last_plan.argtypes = [p, ctypes.POINTER(lin_epi_plan)]
@@ -151,6 +154,12 @@ def lin_epi_pool_weights(handle: int, N: int, K: int, W: int, b: int, pool_kerne
     return load_library().lin_epi_pool_weights(ctypes.c_void_p(handle or None), N, K, ctypes.c_void_p(W or None),
                                                ctypes.c_void_p(b or None), pool_kernel, ctypes.c_void_p(Wp or None),
                                                ctypes.c_void_p(bp or None))
+
+
+def lin_epi_scale_weights(handle: int, N: int, K: int, W: int, b: int, scale: float, Ws: int, bs: int) -> int:
+    return load_library().lin_epi_scale_weights(ctypes.c_void_p(handle or None), N, K, ctypes.c_void_p(W or None),
+                                                ctypes.c_void_p(b or None), float(scale), ctypes.c_void_p(Ws or None),
+                                                ctypes.c_void_p(bs or None))
 
 
 def lin_epi_set_option(handle: int, option: int, value: int) -> int:
@@ -237,6 +246,17 @@ class LinEpi:
     @staticmethod
     def output_shape(M: int, N: int, kind: int) -> tuple:
         return (M,) if kind in (LIN_EPI_POOL_GELU_SCALE_ROWMAX, LIN_EPI_GELU_SCALE_ROWMAX) else (M, N)
+
+    def scale_weights(self, W, b, scale: float):
+        """Tail (a)'s scale folded into new weight and bias tensors."""
+        import torch
+
+        N, K = W.shape
+        Ws = torch.empty_like(W)
+        bs = torch.empty_like(b)
+        rc = lin_epi_scale_weights(self.handle, N, K, W.data_ptr(), b.data_ptr(), scale, Ws.data_ptr(), bs.data_ptr())
+        _check(rc, "lin_epi_scale_weights")
+        return Ws, bs
 
     def pool_weights(self, W, b, pool_kernel: int = 16):
         """Window-averaged weights and bias (device tensors) for tail (b)."""

@@ -511,4 +511,16 @@ __global__ void __launch_bounds__(256) pool_weights_kernel(const float *W, const
     }
 }
 
+// ---------------------------------------------------------------------------
+// Scale-folded weights for tail (a): Ws = scale * W (128-bit, grid-stride
+// over the N*K/4 float4s), bs = scale * b.  HBM-bound.
+__global__ void __launch_bounds__(256) scale_weights_kernel(const float *W, const float *b, float *Ws, float *bs,
+                                                            int64_t nk4, int64_t N, float scale)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nk4; e += stride)
+        reinterpret_cast<f32x4 *>(Ws)[e] = reinterpret_cast<const f32x4 *>(W)[e] * scale;
+    for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < N; n += stride) bs[n] = b[n] * scale;
+}
+
 }  // namespace lin_epi

@@ -573,6 +573,29 @@ int lin_epi_query_plan(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const 
     return LIN_EPI_OK;
 }
 
+int lin_epi_scale_weights(lin_epi_handle h, int64_t N, int64_t K, const float *W, const float *b, float scale,
+                          float *Ws, float *bs)
+{
+    if (!h) return LIN_EPI_EINVAL;
+    if (N < 0 || K < 0) return LIN_EPI_EINVAL;
+    if (N > INT32_MAX || K > INT32_MAX) return LIN_EPI_EINVAL;
+    if (N == 0) return LIN_EPI_OK;
+    if (!b || !bs) return LIN_EPI_EINVAL;
+    if (K > 0 && (!W || !Ws)) return LIN_EPI_EINVAL;
+    if (K % 4 != 0) return LIN_EPI_EALIGN;
+    if (K > 0 && (((uintptr_t)W | (uintptr_t)Ws) & 15u)) return LIN_EPI_EALIGN;
+    if (((uintptr_t)b | (uintptr_t)bs) & 3u) return LIN_EPI_EALIGN;
+    int rc = ensure_device(h);
+    if (rc != LIN_EPI_OK) return rc;
+    const int64_t nk4 = N * K / 4;
+    int64_t blocks = (std::max<int64_t>(nk4, N) + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipStream_t s = h->stream;
+    return timed_launch(h, 2, [&] {
+        hipLaunchKernelGGL(scale_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, s, W, b, Ws, bs, nk4, N, scale);
+    });
+}
+
 int lin_epi_pool_weights(lin_epi_handle h, int64_t N, int64_t K, const float *W, const float *b, int32_t pool_kernel,
                          float *Wp, float *bp)
 {

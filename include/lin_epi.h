@@ -118,6 +118,20 @@ const char *lin_epi_status_string(int status);
 int lin_epi_pool_weights(lin_epi_handle h, int64_t N, int64_t K, const float *W, const float *b,
                          int32_t pool_kernel, float *Wp, float *bp);
 
+/* Weights with tail (a)'s scale folded in, once per weight (page "Kimi-K2.6
+ * l2_p53": scaling the linear output equals a linear layer with scaled
+ * weights and bias, so the multiply can leave the tail):
+ *   Ws[n, k] = scale * W[n, k],  bs[n] = scale * b[n].
+ * Then lin_epi_run(..., Ws, bs, desc with kind 1 and scale 1, Y) gives tail
+ * (a) of the original layer; for a power-of-two scale (the pages' 0.5) the
+ * result is bit-identical, since such scaling commutes with fp32 rounding
+ * (barring overflow and subnormals).  Only tail (a) allows this: tails (b)
+ * and (c) apply their scale after a nonlinearity.  W [N, K], b [N] in;
+ * Ws [N, K], bs [N] out (may equal W, b); device pointers, W and Ws 16-byte
+ * aligned, K a multiple of 4.  Enqueued on the handle's stream. */
+int lin_epi_scale_weights(lin_epi_handle h, int64_t N, int64_t K, const float *W, const float *b, float scale,
+                          float *Ws, float *bs);
+
 /* ---- tuning and introspection (not needed for ordinary use) ------------- */
 
 enum {

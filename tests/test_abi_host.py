@@ -139,6 +139,27 @@ def test_pool_weights_validation(handle, args, expect):
     assert rc == expect, lib.lin_epi_status_string(rc)
 
 
+@pytest.mark.parametrize("args,expect", [
+    (dict(h=None), lib.LIN_EPI_EINVAL),
+    (dict(N=-1), lib.LIN_EPI_EINVAL),
+    (dict(K=-4), lib.LIN_EPI_EINVAL),
+    (dict(b=0), lib.LIN_EPI_EINVAL),
+    (dict(bs=0), lib.LIN_EPI_EINVAL),
+    (dict(W=0), lib.LIN_EPI_EINVAL),
+    (dict(Ws=0), lib.LIN_EPI_EINVAL),
+    (dict(K=6), lib.LIN_EPI_EALIGN),
+    (dict(W=A16 + 4), lib.LIN_EPI_EALIGN),
+    (dict(Ws=A16 + 8), lib.LIN_EPI_EALIGN),
+    (dict(b=A16 + 2), lib.LIN_EPI_EALIGN),
+    (dict(N=0, W=0, b=0, Ws=0, bs=0), lib.LIN_EPI_OK),
+])
+def test_scale_weights_validation(handle, args, expect):
+    a = dict(h=handle, N=64, K=16, W=A16, b=A16, Ws=A16, bs=A16)
+    a.update(args)
+    rc = lib.lin_epi_scale_weights(a["h"], a["N"], a["K"], a["W"], a["b"], 0.5, a["Ws"], a["bs"])
+    assert rc == expect, lib.lin_epi_status_string(rc)
+
+
 def test_destroy_null_is_noop():
     assert lib.lin_epi_destroy(0) == lib.LIN_EPI_OK
 

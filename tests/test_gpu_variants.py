@@ -128,3 +128,33 @@ def test_pool_fold_full_size_checked_rows():
     compare(got[rows], ref, what="pool-fold 1024x8192x8192 (64 rows)")
     # the folded and the direct form agree to fp32 rounding on every row
     compare(got, fused, tol=1e-4, what="pool-fold vs fused direct (all rows)")
+
+
+# ------------------------------------------------- scale folding, tail (a) (f2)
+
+@pytest.mark.parametrize("M,N,K", [(300, 1040, 520), (1000, 6000, 4100), (64, 256, 256)])
+def test_scale_fold_bit_identical_for_power_of_two(M, N, K):
+    """Tail (a) on (0.5 W, 0.5 b) with scale 1 equals tail (a) on (W, b) with
+    scale 0.5 bit for bit (page l2_p53's pre-scaling idea): scaling by a power
+    of two commutes with fp32 rounding.  Both runs use the same plan."""
+    X, W, b = workloads.make_inputs(M, N, K, seed=K + 5)
+    X *= np.float32(6.0)  # make the clamp fire on part of the outputs
+    Xd, Wd, bd = to_dev(X, W, b)
+    t = workloads.TAIL_A
+    with lib.LinEpi() as h:
+        direct = run_gpu(h, Xd, Wd, bd, t)
+        Ws, bs = h.scale_weights(Wd, bd, t.scale)
+        folded = run_gpu(h, Xd, Ws, bs, workloads.Tail(t.kind, scale=1.0, lo=t.lo, hi=t.hi))
+    assert np.array_equal(folded, direct)
+    assert np.array_equal(Ws.cpu().numpy(), W * np.float32(0.5))
+    compare(folded, oracle_rows(X, W, b, t), what="scale-folded tail a %dx%dx%d" % (M, N, K))
+
+
+def test_scale_fold_general_scale_within_tolerance():
+    X, W, b = workloads.make_inputs(200, 300, 260, seed=3)
+    t = workloads.Tail(workloads.SCALE_HARDTANH_GELU, scale=0.3, lo=-1.5, hi=1.0)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        Ws, bs = h.scale_weights(Wd, bd, t.scale)
+        folded = run_gpu(h, Xd, Ws, bs, workloads.Tail(t.kind, scale=1.0, lo=t.lo, hi=t.hi))
+    compare(folded, oracle_rows(X, W, b, t), what="scale-folded tail a, s=0.3")
