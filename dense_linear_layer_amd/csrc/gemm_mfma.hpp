@@ -10,13 +10,14 @@
 // input/weight tiles and a register epilogue.
 //
 // Data flow per workgroup (NT = 64 * WAVES_M * WAVES_N threads):
-//   * global -> registers: 128-bit loads; eight consecutive threads read one
-//     BK=32-float (128-byte) row segment of X or W, so each wavefront load
-//     covers whole cache lines.  Rows past M/N and k past the slice end are
-//     zero-filled (K is a multiple of 4, so a float4 is all-in or all-out).
+//   * global -> registers: 128-bit loads; BK/4 consecutive threads read one
+//     BK-float row segment of X or W (128 bytes for BK = 32, 256 for 64), so
+//     each wavefront load covers whole cache lines.  Rows past M/N and k past
+//     the slice end are zero-filled (K is a multiple of 4, so a float4 is
+//     all-in or all-out).
 //   * registers -> LDS: two stages (double buffer); row stride BK+4 floats,
-//     which makes both the 128-bit stores and the 128-bit fragment reads
-//     bank-conflict free.
+//     so consecutive rows start 4 banks apart, which makes both the 128-bit
+//     stores and the 128-bit fragment reads bank-conflict free.
 //   * LDS -> MFMA operands: the contraction index is permuted inside each
 //     group of 8 k: lane l of a 32x32x2 MFMA supplies k-slot l/32, and the
 //     four MFMAs of one group use components 0..3 of a float4 read at
