@@ -158,3 +158,40 @@ def test_scale_fold_general_scale_within_tolerance():
         Ws, bs = h.scale_weights(Wd, bd, t.scale)
         folded = run_gpu(h, Xd, Ws, bs, workloads.Tail(t.kind, scale=1.0, lo=t.lo, hi=t.hi))
     compare(folded, oracle_rows(X, W, b, t), what="scale-folded tail a, s=0.3")
+
+
+# ------------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("tail", [workloads.TAIL_A, workloads.TAIL_B, workloads.TAIL_C], ids=lambda t: t.name)
+def test_runs_replay_from_a_captured_graph(tail):
+    """lin_epi_run enqueues only kernel launches (no memsets, no allocation
+    once the workspace exists), so a caller can capture it in a HIP graph.
+    One eager run sizes the workspace; the captured graph is then replayed
+    several times with other eager work in between, and every replay must
+    equal the eager result bit for bit.  Split-K is forced so the capture
+    holds both kernels."""
+    X, W, b = workloads.make_inputs(300, 520, 1040, seed=61)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi(stream=s) as h:
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, 3)
+        desc = lib.make_desc(tail.kind, tail.scale, tail.lo, tail.hi, tail.pool_kernel)
+        Y = torch.empty(lib.LinEpi.output_shape(300, 520, tail.kind), dtype=torch.float32, device="cuda:0")
+        with torch.cuda.stream(s):
+            h.run_into(Xd, Wd, bd, desc, Y)
+        s.synchronize()
+        eager = Y.cpu().numpy().copy()
+        assert h.plan().kernels == 2
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            h.run_into(Xd, Wd, bd, desc, Y)
+        for i in range(4):
+            with torch.cuda.stream(s):
+                Y.fill_(float("nan"))
+                torch.cuda.synchronize()
+                g.replay()
+            s.synchronize()
+            assert np.array_equal(Y.cpu().numpy(), eager), "replay %d differs" % i
+            (Xd[:1] * 2).sum().item()  # unrelated eager work between replays
+    compare(eager, oracle_rows(X, W, b, tail), what="graph %s" % tail.name)
