@@ -275,3 +275,26 @@ def test_every_tile_config_all_tails(tile, tail):
         h.set_option(lib.LIN_EPI_OPT_SPLIT_K, 1)
         got = run_gpu(h, *to_dev(X, W, b), tail)
     compare(got, oracle_rows(X, W, b, tail), what="tile %d %s" % (tile, tail.name))
+
+
+# ------------------------------------------------------------- maximum sizes
+
+@pytest.mark.parametrize("tail", [workloads.TAIL_C, workloads.TAIL_B], ids=lambda t: t.name)
+def test_output_beyond_2_to_31_elements(tail):
+    """M x N above 2^31 (an 8.6 GB output for the elementwise tail): every
+    output offset beyond 32 bits must land where the oracle says.  Rows are
+    sampled on the device (the output is never copied whole)."""
+    M, N, K = 65536 + 37, 32768, 68
+    assert M * N > 2**31
+    X, W, b = workloads.make_inputs(M, N, K, seed=77)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        Y = h.run(Xd, Wd, bd, desc_for(tail))
+        torch.cuda.synchronize()
+        p = h.plan()
+        log("plan: tile %dx%d split %d grid %d" % (p.tile_m, p.tile_n, p.split_k, p.grid_main))
+    rows = np.array([0, 1, 65535, 65536, M - 2, M - 1, 40000, 12345])
+    got = Y[torch.from_numpy(rows).to("cuda:0")].cpu().numpy()
+    del Y
+    torch.cuda.empty_cache()
+    compare(got, oracle_rows(X, W, b, tail, rows), what="M*N > 2^31, %s" % tail.name)
