@@ -14,7 +14,8 @@
 //     BK-float row segment of X or W (128 bytes for BK = 32, 256 for 64), so
 //     each wavefront load covers whole cache lines.  Rows past M/N and k past
 //     the slice end are zero-filled (K is a multiple of 4, so a float4 is
-//     all-in or all-out).
+//     all-in or all-out): by the buffer range check where buffer loads are
+//     used, else by predicated loads.
 //   * registers -> LDS: two stages (double buffer); row stride BK+4 floats,
 //     so consecutive rows start 4 banks apart, which makes both the 128-bit
 //     stores and the 128-bit fragment reads bank-conflict free.
@@ -86,16 +87,24 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int &t
 // A workgroup tile shape: BM x BN outputs, K step BK, WAVES_M x WAVES_N
 // wavefronts each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile, and the
 // number of workgroups meant to share one compute unit (register budget).
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WG_PER_CU_>
+// BUFLOAD selects buffer loads for global->register staging where the
+// range-checked form is usable (see gemm_epi_kernel).
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WG_PER_CU_, bool BUFLOAD_ = true>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WG_PER_CU = WG_PER_CU_;
+    static constexpr bool BUFLOAD = BUFLOAD_;
     static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
     static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES_M * WAVES_N / 4;
     static constexpr int LDS_BYTES = 2 * (BM + BN) * (BK + 4) * 4;
 };
 
-template <class Cfg, int EPI>
+// Byte window the buffer-load path is used within: a tile's rows of X or W
+// (rows * K * 4 bytes) must fit below this, which leaves OOB_OFFSET (added to
+// a K offset < 2^31 bytes) out of range and inside 32 bits.
+constexpr int64_t kBufferWindow = 1 << 30;
+
+template <class Cfg, int EPI, bool BUF>
 __global__ void __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD)
 gemm_epi_kernel(GemmArgs a)
 {
@@ -134,7 +143,47 @@ gemm_epi_kernel(GemmArgs a)
 
     f32x4 ra[A_LD], rb[B_LD];
 
+    // Buffer-load staging (BUF): one buffer resource over this tile's rows
+    // of X and one over its rows of W, sized to the valid rows.  A read past
+    // num_records returns zeros in hardware, so rows beyond M or N need no
+    // per-load branch; loop-invariant per-thread byte offsets plus the K
+    // position as the scalar offset address each float4, and the K tail is
+    // masked by swapping in an out-of-range offset.  The host uses this path
+    // only when rows * K * 4 < kBufferWindow.
+    constexpr int OOB_OFFSET = (int)kBufferWindow;
+    const int a_bytes = BUF ? min(BM, M - m0) * K * 4 : 0, b_bytes = BUF ? min(BN, N - n0) * K * 4 : 0;
+    const __amdgpu_buffer_rsrc_t rsA =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.X + (int64_t)m0 * K), (short)0, a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsB =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.W + (int64_t)n0 * K), (short)0, b_bytes, 0x00020000);
+    int offA[A_LD], offB[B_LD], colA[A_LD], colB[B_LD];
+    if constexpr (BUF) {
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            const int idx = tid + i * NT;
+            colA[i] = (idx % C4) * 4;
+            offA[i] = (A_EVEN || idx < BM * C4) ? ((idx / C4) * K + colA[i]) * 4 : OOB_OFFSET;
+        }
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) {
+            const int idx = tid + i * NT;
+            colB[i] = (idx % C4) * 4;
+            offB[i] = (B_EVEN || idx < BN * C4) ? ((idx / C4) * K + colB[i]) * 4 : OOB_OFFSET;
+        }
+    }
+
     auto gload = [&](int k0) {
+        if constexpr (BUF) {
+#pragma unroll
+            for (int i = 0; i < A_LD; ++i)
+                ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, k0 + colA[i] < kend ? offA[i] : OOB_OFFSET, k0 * 4,
+                                                              0);
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i)
+                rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rsB, k0 + colB[i] < kend ? offB[i] : OOB_OFFSET, k0 * 4,
+                                                              0);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
             const int idx = tid + i * NT;
@@ -158,6 +207,7 @@ gemm_epi_kernel(GemmArgs a)
             rb[i] = v;
         }
     };
+    (void)offA, (void)offB, (void)colA, (void)colB;
     auto sstore = [&](int buf) {
         float *As = smem + buf * STAGE;
         float *Bs = As + BM * LDK;

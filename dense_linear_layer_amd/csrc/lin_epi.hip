@@ -29,7 +29,7 @@ using CfgLarge = TileCfg<256, 256, 32, 4, 2, 1>;
 using CfgMid = TileCfg<128, 256, 32, 2, 4, 1>;
 using CfgSmall = TileCfg<128, 128, 32, 2, 2, 2>;
 using CfgTiny = TileCfg<64, 64, 32, 2, 2, 4>;
-using CfgSkinny = TileCfg<32, 256, 64, 1, 8, 1>;
+using CfgSkinny = TileCfg<32, 256, 64, 1, 8, 1, false>;  // plain loads stream W faster here
 
 enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_COUNT = 5 };
 
@@ -138,8 +138,15 @@ int timed_launch(lin_epi_ctx *h, int role, Launch &&launch)
 template <class Cfg, int EPI>
 void launch_gemm_cfg(const GemmArgs &g, int64_t grid_x, int split, hipStream_t s)
 {
-    hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI>), dim3((unsigned)grid_x, (unsigned)split), dim3(Cfg::THREADS), 0, s,
-                       g);
+    const dim3 grid((unsigned)grid_x, (unsigned)split), block(Cfg::THREADS);
+    if constexpr (Cfg::BUFLOAD) {
+        // buffer loads while a tile's rows of X and W span less than the window
+        if ((int64_t)std::max(Cfg::BM, Cfg::BN) * g.K * 4 < kBufferWindow) {
+            hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI, true>), grid, block, 0, s, g);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI, false>), grid, block, 0, s, g);
 }
 
 template <int EPI>

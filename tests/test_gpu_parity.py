@@ -298,3 +298,19 @@ def test_output_beyond_2_to_31_elements(tail):
     del Y
     torch.cuda.empty_cache()
     compare(got, oracle_rows(X, W, b, tail, rows), what="M*N > 2^31, %s" % tail.name)
+
+
+@pytest.mark.parametrize("K", [2**20 - 4, 2**20])
+@pytest.mark.parametrize("split", [1, 3])
+def test_long_k_across_the_buffer_window(K, split):
+    """With 256-row tiles, K = 2^20 is the first length whose tile rows span
+    the buffer-load window (rows * K * 4 bytes = 2^30), so the kernel falls
+    back to predicated loads; K = 2^20 - 4 is the last that uses buffer loads.
+    Integer inputs keep every sum exact (|sum| <= 4 K < 2^24)."""
+    M, N = 3, 37
+    X, W, b = workloads.integer_inputs(M, N, K, seed=K % 1000 + split)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_TILE, 1)
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, split)
+        got = run_gpu(h, *to_dev(X, W, b), workloads.TAIL_NONE)
+    assert np.array_equal(got.astype(np.float64), oracle.linear_rows(X, W, b))
