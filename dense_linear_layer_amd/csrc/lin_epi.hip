@@ -81,6 +81,7 @@ struct lin_epi_ctx {
     bool has_plan = false;
     lin_epi_plan plan{};
     std::vector<PendingTiming> pending;
+    std::vector<hipEvent_t> spare_events;  // recycled by lin_epi_profile_read
     lin_epi_profile prof{};
 };
 
@@ -118,21 +119,46 @@ int ensure_workspace(lin_epi_ctx *h, size_t bytes)
     return LIN_EPI_OK;
 }
 
+// An event for profiling, reused from earlier reads when possible so that a
+// timed launch costs two event records and no event creation.
+int take_event(lin_epi_ctx *h, hipEvent_t *e)
+{
+    if (!h->spare_events.empty()) {
+        *e = h->spare_events.back();
+        h->spare_events.pop_back();
+        return LIN_EPI_OK;
+    }
+    return hipEventCreate(e) == hipSuccess ? LIN_EPI_OK : LIN_EPI_EHIP;
+}
+
 template <typename Launch>
 int timed_launch(lin_epi_ctx *h, int role, Launch &&launch)
 {
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (h->profile) {
-        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return LIN_EPI_EHIP;
-        if (hipEventRecord(e0, h->stream) != hipSuccess) return LIN_EPI_EHIP;
+        if (take_event(h, &e0) != LIN_EPI_OK) return LIN_EPI_EHIP;
+        if (take_event(h, &e1) != LIN_EPI_OK) {
+            h->spare_events.push_back(e0);
+            return LIN_EPI_EHIP;
+        }
+        if (hipEventRecord(e0, h->stream) != hipSuccess) {
+            h->spare_events.push_back(e0);
+            h->spare_events.push_back(e1);
+            return LIN_EPI_EHIP;
+        }
     }
     launch();
-    if (hipGetLastError() != hipSuccess) return LIN_EPI_EHIP;
+    const bool launched = hipGetLastError() == hipSuccess;
     if (h->profile) {
-        if (hipEventRecord(e1, h->stream) != hipSuccess) return LIN_EPI_EHIP;
+        if (!launched || hipEventRecord(e1, h->stream) != hipSuccess) {
+            // e0 may already be recorded; drop both rather than reuse them
+            (void)hipEventDestroy(e0);
+            (void)hipEventDestroy(e1);
+            return LIN_EPI_EHIP;
+        }
         h->pending.push_back({role, e0, e1});
     }
-    return LIN_EPI_OK;
+    return launched ? LIN_EPI_OK : LIN_EPI_EHIP;
 }
 
 template <class Cfg, int EPI>
@@ -339,6 +365,7 @@ int lin_epi_destroy(lin_epi_handle h)
         (void)hipEventDestroy(p.start);
         (void)hipEventDestroy(p.stop);
     }
+    for (hipEvent_t e : h->spare_events) (void)hipEventDestroy(e);
     if (h->ws) (void)hipFree(h->ws);
     delete h;
     return rc;
@@ -390,8 +417,8 @@ int lin_epi_profile_read(lin_epi_handle h, lin_epi_profile *out)
             } else {
                 rc = LIN_EPI_EHIP;
             }
-            (void)hipEventDestroy(p.start);
-            (void)hipEventDestroy(p.stop);
+            h->spare_events.push_back(p.start);
+            h->spare_events.push_back(p.stop);
         }
         h->pending.clear();
     }
