@@ -9,16 +9,21 @@
 // fusion and page "Kimi-K2.6 l2_p59" sketches as a tiled kernel with staged
 // input/weight tiles and a register epilogue.
 //
-// Data flow per workgroup (NT = 64 * WAVES_M * WAVES_N threads):
-//   * global -> registers: 128-bit loads; BK/4 consecutive threads read one
-//     BK-float row segment of X or W (128 bytes for BK = 32, 256 for 64), so
-//     each wavefront load covers whole cache lines.  Rows past M/N and k past
-//     the slice end are zero-filled (K is a multiple of 4, so a float4 is
-//     all-in or all-out): by the buffer range check where buffer loads are
-//     used, else by predicated loads.
-//   * registers -> LDS: two stages (double buffer); row stride BK+4 floats,
-//     so consecutive rows start 4 banks apart, which makes both the 128-bit
-//     stores and the 128-bit fragment reads bank-conflict free.
+// Data flow per workgroup (NT = 64 * WAVES_M * WAVES_N threads), two LDS
+// stages (double buffer), one K step of BK per stage:
+//   * global -> LDS directly (the buffer-load configurations, BK = 32):
+//     buffer_load_dwordx4 ... lds writes each wavefront's 64 x 16 bytes
+//     straight into LDS, 8 rows of 128 bytes per instruction, with the 16-byte
+//     chunks of a row XOR-swizzled so the fragment reads are bank-conflict
+//     free.  No registers and no LDS store instructions are spent on staging,
+//     and a step's loads are issued a whole step ahead of their use.
+//   * otherwise global -> registers -> LDS: 128-bit loads, BK/4 consecutive
+//     threads per BK-float row segment (whole cache lines per wavefront), then
+//     128-bit LDS stores with a row stride of BK+4 floats, so consecutive rows
+//     start 4 banks apart and stores and fragment reads are conflict free.
+//   * Rows past M/N and k past the slice end are zero-filled (K is a multiple
+//     of 4, so a float4 is all-in or all-out): by the buffer range check where
+//     buffer loads are used, else by predicated loads.
 //   * LDS -> MFMA operands: the contraction index is permuted inside each
 //     group of 8 k: lane l of a 32x32x2 MFMA supplies k-slot l/32, and the
 //     four MFMAs of one group use components 0..3 of a float4 read at
@@ -87,8 +92,8 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int &t
 // A workgroup tile shape: BM x BN outputs, K step BK, WAVES_M x WAVES_N
 // wavefronts each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile, and the
 // number of workgroups meant to share one compute unit (register budget).
-// BUFLOAD selects buffer loads for global->register staging where the
-// range-checked form is usable (see gemm_epi_kernel).
+// BUFLOAD selects buffer loads (direct to LDS when BK = 32, else into
+// registers) where the range-checked form is usable (see gemm_epi_kernel).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WG_PER_CU_, bool BUFLOAD_ = true>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -96,7 +101,9 @@ struct TileCfg {
     static constexpr bool BUFLOAD = BUFLOAD_;
     static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
     static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES_M * WAVES_N / 4;
-    static constexpr int LDS_BYTES = 2 * (BM + BN) * (BK + 4) * 4;
+    // Two stages; unpadded 128-byte rows on the direct-to-LDS path (buffer
+    // loads with BK = 32), rows padded to BK + 4 floats otherwise.
+    static constexpr int LDS_BYTES = 2 * (BM + BN) * (BUFLOAD && BK == 32 ? BK : BK + 4) * 4;
 };
 
 // Byte window the buffer-load path is used within: a tile's rows of X or W
@@ -123,7 +130,11 @@ gemm_epi_kernel(GemmArgs a)
     constexpr bool B_EVEN = B_LD * NT == BN * C4;
     static_assert(BK % 8 == 0 && TM % 32 == 0 && TN % 32 == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+    // Direct-to-LDS staging (DMA): buffer loads that write LDS themselves,
+    // for the buffer-load configurations with BK = 32 (one 128-byte row
+    // segment = 8 float4 chunks).
+    constexpr bool DMA = BUF && BK == 32;
+    __shared__ __attribute__((aligned(16))) float smem[DMA ? (BM + BN) * BK : 2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -145,10 +156,11 @@ gemm_epi_kernel(GemmArgs a)
 
     // Buffer-load staging (BUF): one buffer resource over this tile's rows
     // of X and one over its rows of W, sized to the valid rows.  A read past
-    // num_records returns zeros in hardware, so rows beyond M or N need no
-    // per-load branch; loop-invariant per-thread byte offsets plus the K
-    // position as the scalar offset address each float4, and the K tail is
-    // masked by swapping in an out-of-range offset.  The host uses this path
+    // num_records returns zeros in hardware (into LDS as well, for the
+    // direct-to-LDS form), so rows beyond M or N need no per-load branch;
+    // loop-invariant per-thread byte offsets plus the K position as the
+    // scalar offset address each float4, and the K tail is masked by
+    // swapping in an out-of-range offset.  The host uses this path
     // only when rows * K * 4 < kBufferWindow.
     constexpr int OOB_OFFSET = (int)kBufferWindow;
     const int a_bytes = BUF ? min(BM, M - m0) * K * 4 : 0, b_bytes = BUF ? min(BN, N - n0) * K * 4 : 0;
@@ -258,44 +270,124 @@ gemm_epi_kernel(GemmArgs a)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][c], bf[j][c], acc[i][j], 0, 0, 0);
     };
 
-    // Software pipeline over K steps (one LDS stage = BK of K per step):
-    //   * step kt+1's tile is written to the other LDS stage before step kt's
-    //     second-to-last MFMA group, so the stores complete under MFMA work;
-    //   * the registers it came from receive the global loads of step kt+2
-    //     right after that group's MFMAs are issued (the issue slots before
-    //     the barrier are otherwise idle), so the loads have a whole step to
-    //     arrive;
-    //   * the last group's MFMAs are issued after the barrier, together with
-    //     the LDS reads of the next step's first group, so the matrix pipe
-    //     has queued work while the barrier and those reads resolve.
-    // The other stage is free to overwrite: every wavefront finished reading
-    // it before the previous barrier.
-    if (nk > 0) {
-        gload(kbeg);
-        sstore(0);
-        if (nk > 1) gload(kbeg + BK);
-        __syncthreads();
-        read_frags(0, 0, fa[0], fb[0]);
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        const int buf = kt & 1;
+    if constexpr (DMA) {
+        // Each LDS stage holds the tile's BM rows of X then BN rows of W,
+        // 128 bytes per row, unpadded.  One buffer_load ... lds instruction
+        // writes 1 KiB (64 lanes x 16 B) contiguously: a block of 8 rows,
+        // lane l landing at row l/8, physical chunk l%8.  Chunks are stored
+        // XOR-swizzled, physical = logical ^ s(row) with
+        // s(row) = (row % 8) ^ ((row / 8) % 2), so the fragment reads (32
+        // rows, one logical chunk) hit 8 distinct chunk positions per 8 rows
+        // and, with the row parity, 16 distinct 16-byte slots per 16 rows:
+        // no bank conflicts at 128 or 256 bytes per LDS cycle.  Lane l
+        // therefore fetches logical chunk (l%8) ^ s(row) of its row.
+        __shared__ __attribute__((aligned(16))) float smem1[(BM + BN) * BK];
+        constexpr int NW = WAVES_M * WAVES_N;
+        constexpr int NBA = BM / 8, NBB = BN / 8;  // 8-row blocks per stage
+        static_assert(NBA % NW == 0 && NBB % NW == 0 && NW % 2 == 0, "DMA block split");
+        constexpr int NLA = NBA / NW, NL = (NBA + NBB) / NW;  // DMA instructions per wave and step
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        const int lr = lane >> 3;
+        const int cdma = (lane & 7) ^ lr ^ (wave_u & 1);  // blocks i*NW + wave all have parity wave&1
+        // Byte offset of this lane's float4 in operand block i of a stage
+        // (rows counted from the tile's first row of X or of W).
+        const int lane_off = (lr * K + 4 * cdma) * 4;
+        auto dma = [&](float *stage, int k0) {
+            const bool kv = k0 + 4 * cdma < kend;
 #pragma unroll
-        for (int g = 0; g < G - 1; ++g) {
-            read_frags(buf, (g + 1) * 8, fa[(g + 1) & 1], fb[(g + 1) & 1]);
-            if (g == G - 2 && more) sstore(buf ^ 1);
-            mfma_group(fa[g & 1], fb[g & 1]);
-            if (g == G - 2 && kt + 2 < nk) gload(kbeg + (kt + 2) * BK);
+            for (int i = 0; i < NL; ++i) {
+                auto *dst = (__attribute__((address_space(3))) void *)(stage + (i * NW + wave_u) * 256);
+                const int blk = (i < NLA ? i : i - NLA) * NW + wave_u;
+                const int voff = kv ? lane_off + blk * 8 * K * 4 : OOB_OFFSET;
+                if (i < NLA)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, dst, 16, voff, k0 * 4, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, dst, 16, voff, k0 * 4, 0, 0);
+            }
+        };
+        const int tsw = (lane >> 5) ^ (frag_row & 7) ^ ((frag_row >> 3) & 1);
+        auto read_dma = [&](const float *stage, int g, f32x4 (&af)[FM], f32x4 (&bf)[FN]) {
+            const int ch = 4 * ((2 * g) ^ tsw);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const f32x4 *>(stage + (wm * TM + i * 32 + frag_row) * BK + ch);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const f32x4 *>(stage + (BM + wn * TN + j * 32 + frag_row) * BK + ch);
+        };
+        // One K step: the DMA of step kt+1 into the other stage is issued
+        // first (every wavefront finished reading that stage before the
+        // previous barrier), so it has the whole step to land; the wait for
+        // it sits just before the barrier.  The two stages are separate LDS
+        // arrays and the loop is unrolled by two, so the compiler can tell
+        // the DMA target from the stage being read and does not make those
+        // reads wait for it.
+        auto step = [&](float *cur, float *nxt, int kt) {
+            const bool more = kt + 1 < nk;
+            if (more) dma(nxt, kbeg + (kt + 1) * BK);
+#pragma unroll
+            for (int g = 0; g < G - 1; ++g) {
+                read_dma(cur, g + 1, fa[(g + 1) & 1], fb[(g + 1) & 1]);
+                mfma_group(fa[g & 1], fb[g & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA has landed
+            __syncthreads();
+            if (more) read_dma(nxt, 0, fa[G & 1], fb[G & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_group(fa[(G - 1) & 1], fb[(G - 1) & 1]);
+        };
+        if (nk > 0) {
+            dma(smem, kbeg);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            read_dma(smem, 0, fa[0], fb[0]);
         }
-        // Keep the stores and the second-to-last group's MFMAs ahead of the
-        // barrier, and the next step's first LDS reads ahead of the last
-        // group's MFMAs (MFMAs carry no memory dependence, so the scheduler
-        // would otherwise move them across the barrier).
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        if (more) read_frags(buf ^ 1, 0, fa[G & 1], fb[G & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(fa[(G - 1) & 1], fb[(G - 1) & 1]);
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(smem, smem1, kt);
+            if (kt + 1 < nk) step(smem1, smem, kt + 1);
+        }
+    } else {
+        // Software pipeline over K steps (one LDS stage = BK of K per step):
+        //   * step kt+1's tile is written to the other LDS stage before step kt's
+        //     second-to-last MFMA group, so the stores complete under MFMA work;
+        //   * the registers it came from receive the global loads of step kt+2
+        //     right after that group's MFMAs are issued (the issue slots before
+        //     the barrier are otherwise idle), so the loads have a whole step to
+        //     arrive;
+        //   * the last group's MFMAs are issued after the barrier, together with
+        //     the LDS reads of the next step's first group, so the matrix pipe
+        //     has queued work while the barrier and those reads resolve.
+        // The other stage is free to overwrite: every wavefront finished reading
+        // it before the previous barrier.
+        if (nk > 0) {
+            gload(kbeg);
+            sstore(0);
+            if (nk > 1) gload(kbeg + BK);
+            __syncthreads();
+            read_frags(0, 0, fa[0], fb[0]);
+        }
+        for (int kt = 0; kt < nk; ++kt) {
+            const bool more = kt + 1 < nk;
+            const int buf = kt & 1;
+    #pragma unroll
+            for (int g = 0; g < G - 1; ++g) {
+                read_frags(buf, (g + 1) * 8, fa[(g + 1) & 1], fb[(g + 1) & 1]);
+                if (g == G - 2 && more) sstore(buf ^ 1);
+                mfma_group(fa[g & 1], fb[g & 1]);
+                if (g == G - 2 && kt + 2 < nk) gload(kbeg + (kt + 2) * BK);
+            }
+            // Keep the stores and the second-to-last group's MFMAs ahead of the
+            // barrier, and the next step's first LDS reads ahead of the last
+            // group's MFMAs (MFMAs carry no memory dependence, so the scheduler
+            // would otherwise move them across the barrier).
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            if (more) read_frags(buf ^ 1, 0, fa[G & 1], fb[G & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_group(fa[(G - 1) & 1], fb[(G - 1) & 1]);
+        }
+
     }
 
     // ------------------------------------------------------------------ epilogue
