@@ -189,19 +189,21 @@ def main() -> int:
     spot_err = float(np.max(np.abs(got - ref)))
     spot_ok = bool(np.all(np.abs(got - ref) <= 1e-3 * (1 + np.abs(ref))))
 
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the per-step spread comes from the
+    # same timed run as the total
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for _ in range(args.warmup):
         h.run_into(Xd, Wd_run, bd_run, desc, Y)
     torch.cuda.synchronize()
     h.profile()  # discard anything recorded so far
     h.set_option(lib.LIN_EPI_OPT_PROFILE, 1)
-    start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         h.run_into(Xd, Wd_run, bd_run, desc, Y)
-    stop.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    total_ms = marks[0].elapsed_time(marks[-1])
+    step_times = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     prof = h.profile()
     h.set_option(lib.LIN_EPI_OPT_PROFILE, 0)
     plan = h.plan()
@@ -243,6 +245,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_ms": {"median": round(float(np.median(step_times)), 5), "min": round(step_times[0], 5),
+                    "max": round(step_times[-1], 5)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
