@@ -94,17 +94,32 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int &t
 // number of workgroups meant to share one compute unit (register budget).
 // BUFLOAD selects buffer loads (direct to LDS when BK = 32, else into
 // registers) where the range-checked form is usable (see gemm_epi_kernel).
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WG_PER_CU_, bool BUFLOAD_ = true>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WG_PER_CU_, bool BUFLOAD_ = true, int STAGES_ = 2>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WG_PER_CU = WG_PER_CU_;
     static constexpr bool BUFLOAD = BUFLOAD_;
+    static constexpr int STAGES = STAGES_;  // LDS stages of the direct-to-LDS path
     static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
     static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES_M * WAVES_N / 4;
-    // Two stages; unpadded 128-byte rows on the direct-to-LDS path (buffer
-    // loads with BK = 32), rows padded to BK + 4 floats otherwise.
-    static constexpr int LDS_BYTES = 2 * (BM + BN) * (BUFLOAD && BK == 32 ? BK : BK + 4) * 4;
+    // Direct-to-LDS path (buffer loads, BK = 32): STAGES stages of whole
+    // 1 KiB blocks (8 unpadded 128-byte rows), the block count rounded up to
+    // a multiple of the wavefront count.  Otherwise two stages of rows
+    // padded to BK + 4 floats.
+    static constexpr bool DMA = BUFLOAD && BK == 32;
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int DMA_BLOCKS = ((BM + BN) / 8 + NW - 1) / NW * NW;
+    static constexpr int LDS_BYTES = DMA ? STAGES * DMA_BLOCKS * 1024 : 2 * (BM + BN) * (BK + 4) * 4;
 };
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt
+// and lgkmcnt left at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Byte window the buffer-load path is used within: a tile's rows of X or W
 // (rows * K * 4 bytes) must fit below this, which leaves OOB_OFFSET (added to
@@ -132,9 +147,10 @@ gemm_epi_kernel(GemmArgs a)
 
     // Direct-to-LDS staging (DMA): buffer loads that write LDS themselves,
     // for the buffer-load configurations with BK = 32 (one 128-byte row
-    // segment = 8 float4 chunks).
-    constexpr bool DMA = BUF && BK == 32;
-    __shared__ __attribute__((aligned(16))) float smem[DMA ? (BM + BN) * BK : 2 * STAGE];
+    // segment = 8 float4 chunks).  smem is stage 0 there.
+    constexpr bool DMA = BUF && Cfg::DMA;
+    constexpr int DMA_STAGE = Cfg::DMA_BLOCKS * 256;  // floats per DMA stage
+    __shared__ __attribute__((aligned(16))) float smem[DMA ? DMA_STAGE : 2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -272,81 +288,111 @@ gemm_epi_kernel(GemmArgs a)
 
     if constexpr (DMA) {
         // Each LDS stage holds the tile's BM rows of X then BN rows of W,
-        // 128 bytes per row, unpadded.  One buffer_load ... lds instruction
-        // writes 1 KiB (64 lanes x 16 B) contiguously: a block of 8 rows,
-        // lane l landing at row l/8, physical chunk l%8.  Chunks are stored
-        // XOR-swizzled, physical = logical ^ s(row) with
-        // s(row) = (row % 8) ^ ((row / 8) % 2), so the fragment reads (32
-        // rows, one logical chunk) hit 8 distinct chunk positions per 8 rows
-        // and, with the row parity, 16 distinct 16-byte slots per 16 rows:
-        // no bank conflicts at 128 or 256 bytes per LDS cycle.  Lane l
-        // therefore fetches logical chunk (l%8) ^ s(row) of its row.
-        __shared__ __attribute__((aligned(16))) float smem1[(BM + BN) * BK];
-        constexpr int NW = WAVES_M * WAVES_N;
-        constexpr int NBA = BM / 8, NBB = BN / 8;  // 8-row blocks per stage
-        static_assert(NBA % NW == 0 && NBB % NW == 0 && NW % 2 == 0, "DMA block split");
-        constexpr int NLA = NBA / NW, NL = (NBA + NBB) / NW;  // DMA instructions per wave and step
+        // 128 bytes per row, unpadded, then (when the block count is not a
+        // multiple of the wavefront count) padding blocks.  One
+        // buffer_load ... lds instruction writes 1 KiB (64 lanes x 16 B)
+        // contiguously: a block of 8 rows, lane l landing at row l/8,
+        // physical chunk l%8.  Chunks are stored XOR-swizzled,
+        // physical = logical ^ s(row) with s(row) = (row % 8) ^ ((row / 8) % 2),
+        // so the fragment reads (32 rows, one logical chunk) hit 8 distinct
+        // chunk positions per 8 rows and, with the row parity, 16 distinct
+        // 16-byte slots per 16 rows: no bank conflicts at 128 or 256 bytes per
+        // LDS cycle.  Lane l therefore fetches logical chunk (l%8) ^ s(row).
+        constexpr int NST = Cfg::STAGES;
+        static_assert(NST >= 2 && NST <= 4, "2 to 4 DMA stages");
+        __shared__ __attribute__((aligned(16))) float smem1[DMA_STAGE];
+        __shared__ __attribute__((aligned(16))) float smem2[NST > 2 ? DMA_STAGE : 4];
+        __shared__ __attribute__((aligned(16))) float smem3[NST > 3 ? DMA_STAGE : 4];
+        auto stage = [&](int st) -> float * { return st == 0 ? smem : st == 1 ? smem1 : st == 2 ? smem2 : smem3; };
+        constexpr int NW = Cfg::NW;
+        constexpr int NBA = BM / 8, NB = (BM + BN) / 8;  // 8-row blocks of X, of X and W
+        constexpr int NL = Cfg::DMA_BLOCKS / NW;          // DMA instructions per wavefront and step
+        static_assert(NW % 2 == 0 && NBA % 2 == 0, "block parity = wavefront parity");
         const int wave_u = __builtin_amdgcn_readfirstlane(wave);
         const int lr = lane >> 3;
         const int cdma = (lane & 7) ^ lr ^ (wave_u & 1);  // blocks i*NW + wave all have parity wave&1
-        // Byte offset of this lane's float4 in operand block i of a stage
-        // (rows counted from the tile's first row of X or of W).
+        // Byte offset of this lane's float4 inside an 8-row block of X or W.
         const int lane_off = (lr * K + 4 * cdma) * 4;
-        auto dma = [&](float *stage, int k0) {
-            const bool kv = k0 + 4 * cdma < kend;
+        // Loads of K step k0 into stage st.  Past the slice end every lane is
+        // out of range: the stage gets zeros and no memory is read.
+        auto dma = [&](float *st, int k0) {
+            // the block's row offset and k0 are wave-uniform: scalar offset
+            // (the range check applies to the sum)
+            const int voff = k0 + 4 * cdma < kend ? lane_off : OOB_OFFSET;
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                auto *dst = (__attribute__((address_space(3))) void *)(stage + (i * NW + wave_u) * 256);
-                const int blk = (i < NLA ? i : i - NLA) * NW + wave_u;
-                const int voff = kv ? lane_off + blk * 8 * K * 4 : OOB_OFFSET;
-                if (i < NLA)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, dst, 16, voff, k0 * 4, 0, 0);
-                else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, dst, 16, voff, k0 * 4, 0, 0);
+                const int blk = i * NW + wave_u;
+                auto *dst = (__attribute__((address_space(3))) void *)(st + blk * 256);
+                const bool all_a = (i + 1) * NW <= NBA, all_b = i * NW >= NBA && (i + 1) * NW <= NB;
+                if (all_a || (!all_b && blk < NBA)) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, dst, 16, voff, (blk * 8 * K + k0) * 4, 0, 0);
+                } else if (all_b || blk < NB) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, dst, 16, voff, ((blk - NBA) * 8 * K + k0) * 4, 0, 0);
+                } else {  // padding block: zeros, never read
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, dst, 16, OOB_OFFSET, 0, 0, 0);
+                }
             }
         };
         const int tsw = (lane >> 5) ^ (frag_row & 7) ^ ((frag_row >> 3) & 1);
-        auto read_dma = [&](const float *stage, int g, f32x4 (&af)[FM], f32x4 (&bf)[FN]) {
+        auto read_dma = [&](const float *st, int g, f32x4 (&af)[FM], f32x4 (&bf)[FN]) {
             const int ch = 4 * ((2 * g) ^ tsw);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const f32x4 *>(stage + (wm * TM + i * 32 + frag_row) * BK + ch);
+                af[i] = *reinterpret_cast<const f32x4 *>(st + (wm * TM + i * 32 + frag_row) * BK + ch);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const f32x4 *>(stage + (BM + wn * TN + j * 32 + frag_row) * BK + ch);
+                bf[j] = *reinterpret_cast<const f32x4 *>(st + (BM + wn * TN + j * 32 + frag_row) * BK + ch);
         };
-        // One K step: the DMA of step kt+1 into the other stage is issued
-        // first (every wavefront finished reading that stage before the
-        // previous barrier), so it has the whole step to land; the wait for
-        // it sits just before the barrier.  The two stages are separate LDS
-        // arrays and the loop is unrolled by two, so the compiler can tell
-        // the DMA target from the stage being read and does not make those
-        // reads wait for it.
-        auto step = [&](float *cur, float *nxt, int kt) {
-            const bool more = kt + 1 < nk;
-            if (more) dma(nxt, kbeg + (kt + 1) * BK);
+        // One K step kt (stage kt % NST): the DMA of step kt+NST-1 goes into
+        // the stage step kt-1 used (every wavefront finished reading it before
+        // the previous barrier), so loads are issued NST-1 steps ahead; before
+        // the barrier, a wait until at most the NST-2 younger steps' loads are
+        // outstanding, i.e. step kt+1 has landed (loads complete in order).
+        // The DMA instructions are spread over the first group's MFMAs (one
+        // per 4*FM*FN/NL MFMAs): issued back to back they would hold every
+        // wavefront of the CU off the matrix pipes at the same moment, right
+        // after the barrier.  The stages are separate LDS arrays and the loop
+        // is unrolled by NST, so the compiler can tell a DMA target from the
+        // stage being read and does not make those reads wait for the DMA.
+        auto step = [&](float *cur, float *nxt, float *fre, int kt) {
+            dma(fre, kbeg + (kt + NST - 1) * BK);
+            read_dma(cur, 1, fa[1], fb[1]);
+            mfma_group(fa[0], fb[0]);
+            // scheduling groups (masks: 0x100 LDS reads, 0x008 MFMA, 0x020
+            // vector-memory reads): the next group's fragment reads first,
+            // then MFMAs and DMA instructions alternating
+            __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
 #pragma unroll
-            for (int g = 0; g < G - 1; ++g) {
+            for (int q = 0; q < NL; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * FM * FN / NL, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 1; g < G - 1; ++g) {
                 read_dma(cur, g + 1, fa[(g + 1) & 1], fb[(g + 1) & 1]);
                 mfma_group(fa[g & 1], fb[g & 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA has landed
+            wait_vmcnt<(NST - 2) * NL>();
             __syncthreads();
-            if (more) read_dma(nxt, 0, fa[G & 1], fb[G & 1]);
+            if (kt + 1 < nk) read_dma(nxt, 0, fa[G & 1], fb[G & 1]);
             __builtin_amdgcn_sched_barrier(0);
             mfma_group(fa[(G - 1) & 1], fb[(G - 1) & 1]);
         };
         if (nk > 0) {
-            dma(smem, kbeg);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+            for (int st = 0; st < NST - 1; ++st) dma(stage(st), kbeg + st * BK);
+            wait_vmcnt<(NST - 2) * NL>();
             __syncthreads();
             read_dma(smem, 0, fa[0], fb[0]);
         }
-        for (int kt = 0; kt < nk; kt += 2) {
-            step(smem, smem1, kt);
-            if (kt + 1 < nk) step(smem1, smem, kt + 1);
+        for (int kt0 = 0; kt0 < nk; kt0 += NST) {
+#pragma unroll
+            for (int u = 0; u < NST; ++u)
+                if (kt0 + u < nk) step(stage(u), stage((u + 1) % NST), stage((u + NST - 1) % NST), kt0 + u);
         }
+        wait_vmcnt<0>();  // the zero-filling loads past the end have landed before LDS is reused
     } else {
         // Software pipeline over K steps (one LDS stage = BK of K per step):
         //   * step kt+1's tile is written to the other LDS stage before step kt's
