@@ -185,10 +185,10 @@ def test_planner_choices_for_the_workloads(handle):
     assert _plan(handle, 2048, 8192, 8192, A) == (256, 256, 1, 1, 256, 0)
     # 128x32768x32768: 128x256 tiles (128 of them) split in two
     assert _plan(handle, 128, 32768, 32768, C)[:4] == (128, 256, 2, 2)
-    # ragged: 8x24 tiles of 128x256, four K slices -> 768 workgroups = 3 rounds
-    assert _plan(handle, 1000, 6000, 4100, A)[:5] == (128, 256, 4, 2, 768)
-    # pooled-weight tail (b): a 1024x512x8192 GEMM needs 16 slices to fill the device
-    assert _plan(handle, 1024, 512, 8192, F)[:4] == (128, 256, 16, 2)
+    # ragged: 8x47 tiles of 128x128 (two per compute unit), two K slices -> 752 workgroups
+    assert _plan(handle, 1000, 6000, 4100, A)[:5] == (128, 128, 2, 2, 752)
+    # pooled-weight tail (b): a 1024x512x8192 GEMM is split into 8 K slices to fill the device
+    assert _plan(handle, 1024, 512, 8192, F)[:4] == (128, 128, 8, 2)
     # tail (b) unsplit keeps per-tile row maxima: M * tiles_n floats
     t = _plan(handle, 1024, 8192, 8192, B)
     if t[2] == 1:
