@@ -11,8 +11,9 @@ steps on the handle's stream, bracketed by device synchronisation.  Prints
 one JSON line.
 
 The "roofline" object times the dominant (GEMM) kernel with HIP events the
-library records around each launch on its own stream, over the same timed
-steps.  The "cpu_baseline" object times the CPU oracle (as it is, unmodified)
+library records around each launch on its own stream, over K more steps run
+right after the timed ones (the event records would add a few microseconds
+per launch to the timed steps).  The "cpu_baseline" object times the CPU oracle (as it is, unmodified)
 on a bounded sample of rows of the same workload, on this host's cores.
 """
 
@@ -195,8 +196,6 @@ def main() -> int:
     for _ in range(args.warmup):
         h.run_into(Xd, Wd_run, bd_run, desc, Y)
     torch.cuda.synchronize()
-    h.profile()  # discard anything recorded so far
-    h.set_option(lib.LIN_EPI_OPT_PROFILE, 1)
     marks[0].record(stream)
     for i in range(args.steps):
         h.run_into(Xd, Wd_run, bd_run, desc, Y)
@@ -204,6 +203,14 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = marks[0].elapsed_time(marks[-1])
     step_times = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    # per-kernel durations: the same K steps once more, right away (clock
+    # still up), with the library's HIP events around every kernel on its
+    # stream; kept out of the timed steps, where the extra event records add
+    # 4-8 us per kernel launch to the step time
+    h.profile()  # discard anything recorded so far
+    h.set_option(lib.LIN_EPI_OPT_PROFILE, 1)
+    for _ in range(args.steps):
+        h.run_into(Xd, Wd_run, bd_run, desc, Y)
     prof = h.profile()
     h.set_option(lib.LIN_EPI_OPT_PROFILE, 0)
     plan = h.plan()
