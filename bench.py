@@ -105,6 +105,8 @@ def main() -> int:
     ap.add_argument("--split-k", type=int, default=0, help="0 auto, 1 off, S>=2 forced")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reg-staging", action="store_true",
+                    help="ablation: stage operand tiles through registers instead of direct-to-LDS loads")
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused ablation (GEMM to memory, then a separate tail kernel)")
     ap.add_argument("--pool-fold", action="store_true",
@@ -144,6 +146,7 @@ def main() -> int:
     h = lib.LinEpi(stream=stream)
     h.set_option(lib.LIN_EPI_OPT_SPLIT_K, args.split_k)
     h.set_option(lib.LIN_EPI_OPT_UNFUSED, 1 if args.unfused else 0)
+    h.set_option(lib.LIN_EPI_OPT_REG_STAGING, 1 if args.reg_staging else 0)
     flops = float(w.flops)
     prep_ms = None
     if args.pool_fold:
@@ -268,7 +271,7 @@ def main() -> int:
             "kernels_per_step": plan.kernels,
             "frac_of_fp32_mfma_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
             "variant": ("pool_fold" if args.pool_fold else "scale_fold" if args.scale_fold
-                        else "unfused" if args.unfused else "fused"),
+                        else "unfused" if args.unfused else "reg_staging" if args.reg_staging else "fused"),
         },
         "roofline": roofline,
         "parity_spot_check": {"rows": 4, "max_abs_err": spot_err, "ok": spot_ok},

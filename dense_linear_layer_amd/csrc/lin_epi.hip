@@ -84,6 +84,7 @@ struct lin_epi_ctx {
     int64_t tile_opt = 0;
     bool profile = false;
     bool unfused = false;
+    bool reg_staging = false;
     bool has_plan = false;
     lin_epi_plan plan{};
     std::vector<PendingTiming> pending;
@@ -167,13 +168,15 @@ int timed_launch(lin_epi_ctx *h, int role, Launch &&launch)
     return launched ? LIN_EPI_OK : LIN_EPI_EHIP;
 }
 
+// reg_staging: stage operands through registers even where the buffer-load
+// (direct-to-LDS) path is usable (LIN_EPI_OPT_REG_STAGING).
 template <class Cfg, int EPI>
-void launch_gemm_cfg(const GemmArgs &g, int64_t grid_x, int split, hipStream_t s)
+void launch_gemm_cfg(const GemmArgs &g, int64_t grid_x, int split, hipStream_t s, bool reg_staging)
 {
     const dim3 grid((unsigned)grid_x, (unsigned)split), block(Cfg::THREADS);
     if constexpr (Cfg::BUFLOAD) {
         // buffer loads while a tile's rows of X and W span less than the window
-        if ((int64_t)std::max(Cfg::BM, Cfg::BN) * g.K * 4 < kBufferWindow) {
+        if (!reg_staging && (int64_t)std::max(Cfg::BM, Cfg::BN) * g.K * 4 < kBufferWindow) {
             hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI, true>), grid, block, 0, s, g);
             return;
         }
@@ -182,14 +185,14 @@ void launch_gemm_cfg(const GemmArgs &g, int64_t grid_x, int split, hipStream_t s
 }
 
 template <int EPI>
-void launch_gemm(int cfg, const GemmArgs &g, int64_t grid_x, int split, hipStream_t s)
+void launch_gemm(int cfg, const GemmArgs &g, int64_t grid_x, int split, hipStream_t s, bool reg_staging)
 {
     switch (cfg) {
-        case CFG_LARGE: launch_gemm_cfg<CfgLarge, EPI>(g, grid_x, split, s); break;
-        case CFG_MID: launch_gemm_cfg<CfgMid, EPI>(g, grid_x, split, s); break;
-        case CFG_SMALL: launch_gemm_cfg<CfgSmall, EPI>(g, grid_x, split, s); break;
-        case CFG_TINY: launch_gemm_cfg<CfgTiny, EPI>(g, grid_x, split, s); break;
-        default: launch_gemm_cfg<CfgSkinny, EPI>(g, grid_x, split, s); break;
+        case CFG_LARGE: launch_gemm_cfg<CfgLarge, EPI>(g, grid_x, split, s, reg_staging); break;
+        case CFG_MID: launch_gemm_cfg<CfgMid, EPI>(g, grid_x, split, s, reg_staging); break;
+        case CFG_SMALL: launch_gemm_cfg<CfgSmall, EPI>(g, grid_x, split, s, reg_staging); break;
+        case CFG_TINY: launch_gemm_cfg<CfgTiny, EPI>(g, grid_x, split, s, reg_staging); break;
+        default: launch_gemm_cfg<CfgSkinny, EPI>(g, grid_x, split, s, reg_staging); break;
     }
 }
 
@@ -397,6 +400,10 @@ int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value)
             if (value != 0 && value != 1) return LIN_EPI_EINVAL;
             h->unfused = value != 0;
             return LIN_EPI_OK;
+        case LIN_EPI_OPT_REG_STAGING:
+            if (value != 0 && value != 1) return LIN_EPI_EINVAL;
+            h->reg_staging = value != 0;
+            return LIN_EPI_OK;
         default: return LIN_EPI_EINVAL;
     }
 }
@@ -480,7 +487,7 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         rc = ensure_workspace(h, bytes);
         if (rc != LIN_EPI_OK) return rc;
         g.out = static_cast<float *>(h->ws);
-        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s); });
+        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s, h->reg_staging); });
         if (rc != LIN_EPI_OK) return rc;
         const float *P = static_cast<const float *>(h->ws);
         const int32_t pool = kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1;
@@ -500,9 +507,9 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         g.out = static_cast<float *>(h->ws);
         rc = timed_launch(h, 0, [&] {
             if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX)
-                launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s);
+                launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s, h->reg_staging);
             else
-                launch_gemm<EPI_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s);
+                launch_gemm<EPI_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s, h->reg_staging);
         });
         if (rc != LIN_EPI_OK) return rc;
         const float *part = static_cast<const float *>(h->ws);
@@ -517,7 +524,7 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         rc = ensure_workspace(h, bytes);
         if (rc != LIN_EPI_OK) return rc;
         g.out = static_cast<float *>(h->ws);
-        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s); });
+        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s, h->reg_staging); });
         if (rc != LIN_EPI_OK) return rc;
         const float *P = static_cast<const float *>(h->ws);
         rc = timed_launch(h, 1, [&] {
@@ -534,9 +541,9 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         g.out = Y;
         rc = timed_launch(h, 0, [&] {
             switch (kind) {
-                case LIN_EPI_NONE: launch_gemm<EPI_NONE>(pl.cfg, g, tiles, 1, s); break;
-                case LIN_EPI_SCALE_HARDTANH_GELU: launch_gemm<EPI_SCALE_HARDTANH_GELU>(pl.cfg, g, tiles, 1, s); break;
-                default: launch_gemm<EPI_SWISH_SCALE>(pl.cfg, g, tiles, 1, s); break;
+                case LIN_EPI_NONE: launch_gemm<EPI_NONE>(pl.cfg, g, tiles, 1, s, h->reg_staging); break;
+                case LIN_EPI_SCALE_HARDTANH_GELU: launch_gemm<EPI_SCALE_HARDTANH_GELU>(pl.cfg, g, tiles, 1, s, h->reg_staging); break;
+                default: launch_gemm<EPI_SWISH_SCALE>(pl.cfg, g, tiles, 1, s, h->reg_staging); break;
             }
         });
         if (rc != LIN_EPI_OK) return rc;
@@ -555,13 +562,13 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         float *Yraw = rowmax ? ws + part_floats : Y;
         if (split > 1) {
             g.out = ws;
-            rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s); });
+            rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s, h->reg_staging); });
             if (rc != LIN_EPI_OK) return rc;
             rc = timed_launch(h, 1, [&] { launch_reduce<EPI_NONE>(ws, b, Yraw, MN, (int)N, split, g.tail, s); });
             if (rc != LIN_EPI_OK) return rc;
         } else {
             g.out = Yraw;
-            rc = timed_launch(h, 0, [&] { launch_gemm<EPI_NONE>(pl.cfg, g, tiles, 1, s); });
+            rc = timed_launch(h, 0, [&] { launch_gemm<EPI_NONE>(pl.cfg, g, tiles, 1, s, h->reg_staging); });
             if (rc != LIN_EPI_OK) return rc;
         }
         if (rowmax) {

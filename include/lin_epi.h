@@ -153,7 +153,13 @@ enum {
      * wavefronts, 2 = 128x256 with 8, 3 = 128x128 with 4, 4 = 64x64 with 4,
      * 5 = 32x256 with 8 (few rows, weight streaming).
      * The split-K choice is still made (or forced) as usual. */
-    LIN_EPI_OPT_TILE = 4
+    LIN_EPI_OPT_TILE = 4,
+    /* 1 = stage X and W tiles through registers (128-bit loads, then LDS
+     * stores) even where the default direct-to-LDS buffer loads are usable;
+     * 0 = automatic (default).  Both stagings feed the same MFMA sequence,
+     * so results are bit-identical; exists to test and measure the
+     * direct-to-LDS path against the other one. */
+    LIN_EPI_OPT_REG_STAGING = 5
 };
 
 int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value);

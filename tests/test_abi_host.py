@@ -102,6 +102,9 @@ def test_options_and_introspection_validation(handle):
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 2) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 1) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_UNFUSED, 0) == lib.LIN_EPI_OK
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_REG_STAGING, 2) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_REG_STAGING, 1) == lib.LIN_EPI_OK
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_REG_STAGING, 0) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 6) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, -1) == lib.LIN_EPI_EINVAL
     for t in range(6):

@@ -277,6 +277,28 @@ def test_every_tile_config_all_tails(tile, tail):
     compare(got, oracle_rows(X, W, b, tail), what="tile %d %s" % (tile, tail.name))
 
 
+@pytest.mark.parametrize("split", [1, 3])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("tail", ALL_TAILS, ids=lambda t: t.name)
+def test_direct_to_lds_equals_register_staging(tile, split, tail):
+    """The 32-deep-K tiles stage operands with direct-to-LDS buffer loads into
+    a swizzled layout by default; forced register staging (padded rows) must
+    give bit-identical results on random inputs, ragged in M, N and K, since
+    both feed the same MFMA sequence.  Also checked against the oracle."""
+    M, N, K = 261, 530, 1000
+    X, W, b = workloads.make_inputs(M, N, K, seed=100 * tile + split)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_TILE, tile)
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, split)
+        direct = run_gpu(h, Xd, Wd, bd, tail)
+        h.set_option(lib.LIN_EPI_OPT_REG_STAGING, 1)
+        staged = run_gpu(h, Xd, Wd, bd, tail)
+        assert h.plan().split_k == split
+    assert np.array_equal(direct, staged), "staging paths differ (tile %d split %d %s)" % (tile, split, tail.name)
+    compare(direct, oracle_rows(X, W, b, tail), what="tile %d split %d %s" % (tile, split, tail.name))
+
+
 # ------------------------------------------------------------- maximum sizes
 
 @pytest.mark.parametrize("tail", [workloads.TAIL_C, workloads.TAIL_B], ids=lambda t: t.name)
