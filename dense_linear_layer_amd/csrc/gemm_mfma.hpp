@@ -92,8 +92,9 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int &t
 // A workgroup tile shape: BM x BN outputs, K step BK, WAVES_M x WAVES_N
 // wavefronts each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile, and the
 // number of workgroups meant to share one compute unit (register budget).
-// BUFLOAD selects buffer loads (direct to LDS when BK = 32, else into
-// registers) where the range-checked form is usable (see gemm_epi_kernel).
+// BUFLOAD selects direct-to-LDS buffer loads (BK = 32 only) where the
+// range-checked form is usable (see gemm_epi_kernel); otherwise, and for
+// tiles too large for the buffer window, operands go through registers.
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WG_PER_CU_, bool BUFLOAD_ = true, int STAGES_ = 2>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -102,11 +103,12 @@ struct TileCfg {
     static constexpr int STAGES = STAGES_;  // LDS stages of the direct-to-LDS path
     static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
     static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES_M * WAVES_N / 4;
-    // Direct-to-LDS path (buffer loads, BK = 32): STAGES stages of whole
+    // Direct-to-LDS path: STAGES stages of whole
     // 1 KiB blocks (8 unpadded 128-byte rows), the block count rounded up to
     // a multiple of the wavefront count.  Otherwise two stages of rows
     // padded to BK + 4 floats.
-    static constexpr bool DMA = BUFLOAD && BK == 32;
+    static constexpr bool DMA = BUFLOAD;
+    static_assert(!BUFLOAD || BK == 32, "the direct-to-LDS layout holds 128-byte rows");
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int DMA_BLOCKS = ((BM + BN) / 8 + NW - 1) / NW * NW;
     static constexpr int LDS_BYTES = DMA ? STAGES * DMA_BLOCKS * 1024 : 2 * (BM + BN) * (BK + 4) * 4;
@@ -122,8 +124,10 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 
 // Byte window the buffer-load path is used within: a tile's rows of X or W
-// (rows * K * 4 bytes) must fit below this, which leaves OOB_OFFSET (added to
-// a K offset < 2^31 bytes) out of range and inside 32 bits.
+// span rows * K * 4 < 2^30 bytes, so every byte offset the kernel forms
+// (per-lane offset + scalar offset, the latter a row-block offset plus the K
+// position) stays below 2^31, and OOB_OFFSET = 2^30 plus any scalar offset
+// is past num_records yet still inside 32 bits.
 constexpr int64_t kBufferWindow = 1 << 30;
 
 template <class Cfg, int EPI, bool BUF>
@@ -146,9 +150,10 @@ gemm_epi_kernel(GemmArgs a)
     static_assert(BK % 8 == 0 && TM % 32 == 0 && TN % 32 == 0, "tile shape");
 
     // Direct-to-LDS staging (DMA): buffer loads that write LDS themselves,
-    // for the buffer-load configurations with BK = 32 (one 128-byte row
+    // for the buffer-load configurations, all with BK = 32 (one 128-byte row
     // segment = 8 float4 chunks).  smem is stage 0 there.
-    constexpr bool DMA = BUF && Cfg::DMA;
+    constexpr bool DMA = BUF;
+    static_assert(!BUF || Cfg::DMA, "buffer loads are used on the direct-to-LDS path only");
     constexpr int DMA_STAGE = Cfg::DMA_BLOCKS * 256;  // floats per DMA stage
     __shared__ __attribute__((aligned(16))) float smem[DMA ? DMA_STAGE : 2 * STAGE];
 
@@ -170,48 +175,22 @@ gemm_epi_kernel(GemmArgs a)
 
     f32x4 ra[A_LD], rb[B_LD];
 
-    // Buffer-load staging (BUF): one buffer resource over this tile's rows
+    // Direct-to-LDS staging (BUF): one buffer resource over this tile's rows
     // of X and one over its rows of W, sized to the valid rows.  A read past
-    // num_records returns zeros in hardware (into LDS as well, for the
-    // direct-to-LDS form), so rows beyond M or N need no per-load branch;
-    // loop-invariant per-thread byte offsets plus the K position as the
-    // scalar offset address each float4, and the K tail is masked by
-    // swapping in an out-of-range offset.  The host uses this path
-    // only when rows * K * 4 < kBufferWindow.
+    // num_records returns zeros in hardware (written into LDS as zeros), so
+    // rows beyond M or N need no per-load branch, and the K tail is masked by
+    // swapping in an out-of-range offset.  The host uses this path only when
+    // rows * K * 4 < kBufferWindow.
     constexpr int OOB_OFFSET = (int)kBufferWindow;
     const int a_bytes = BUF ? min(BM, M - m0) * K * 4 : 0, b_bytes = BUF ? min(BN, N - n0) * K * 4 : 0;
     const __amdgpu_buffer_rsrc_t rsA =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.X + (int64_t)m0 * K), (short)0, a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsB =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.W + (int64_t)n0 * K), (short)0, b_bytes, 0x00020000);
-    int offA[A_LD], offB[B_LD], colA[A_LD], colB[B_LD];
-    if constexpr (BUF) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int idx = tid + i * NT;
-            colA[i] = (idx % C4) * 4;
-            offA[i] = (A_EVEN || idx < BM * C4) ? ((idx / C4) * K + colA[i]) * 4 : OOB_OFFSET;
-        }
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int idx = tid + i * NT;
-            colB[i] = (idx % C4) * 4;
-            offB[i] = (B_EVEN || idx < BN * C4) ? ((idx / C4) * K + colB[i]) * 4 : OOB_OFFSET;
-        }
-    }
 
+    // Register staging (!BUF): predicated 128-bit loads, zero-filled past M,
+    // N and the slice end.
     auto gload = [&](int k0) {
-        if constexpr (BUF) {
-#pragma unroll
-            for (int i = 0; i < A_LD; ++i)
-                ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, k0 + colA[i] < kend ? offA[i] : OOB_OFFSET, k0 * 4,
-                                                              0);
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i)
-                rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rsB, k0 + colB[i] < kend ? offB[i] : OOB_OFFSET, k0 * 4,
-                                                              0);
-            return;
-        }
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
             const int idx = tid + i * NT;
@@ -235,7 +214,6 @@ gemm_epi_kernel(GemmArgs a)
             rb[i] = v;
         }
     };
-    (void)offA, (void)offB, (void)colA, (void)colB;
     auto sstore = [&](int buf) {
         float *As = smem + buf * STAGE;
         float *Bs = As + BM * LDK;
