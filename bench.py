@@ -118,7 +118,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
         return 2
     if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
