@@ -36,7 +36,7 @@ LIN_EPI_OPT_PROFILE = 2
 LIN_EPI_OPT_UNFUSED = 3
 LIN_EPI_OPT_TILE = 4
 LIN_EPI_OPT_REG_STAGING = 5
-TILE_CONFIGS = {1: (256, 256), 2: (128, 256), 3: (128, 128), 4: (64, 64), 5: (32, 256)}
+TILE_CONFIGS = {1: (256, 256), 2: (128, 256), 3: (128, 128), 4: (64, 64), 5: (32, 128)}
 
 # every function include/lin_epi.h declares
 EXPORTS = (

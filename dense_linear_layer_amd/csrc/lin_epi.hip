@@ -16,7 +16,7 @@ namespace {
 
 // Tile table.  All use v_mfma_f32_32x32x2_f32 and two LDS stages; they
 // differ in workgroup tile and wavefront count, and the dispatcher picks one
-// per call (choose_plan below).  The first four stage 32-deep K steps with
+// per call (choose_plan below).  All stage 32-deep K steps with
 // direct-to-LDS buffer loads (LDS figures below; rows padded to 36 floats,
 // 12 % more, on the register-staged path used when a tile's rows of X or W
 // span 1 GiB or more):
@@ -24,16 +24,16 @@ namespace {
 //   MID    128x256, 8 wavefronts (2x4, 64x64 each),   96 KiB LDS, 1 WG/CU
 //   SMALL  128x128, 4 wavefronts (2x2, 64x64 each),   64 KiB LDS, 2 WG/CU
 //   TINY    64x64,  4 wavefronts (2x2, 32x32 each),   32 KiB LDS, 4 WG/CU
-//   SKINNY  32x256, 8 wavefronts (1x8, 32x32 each),  153 KiB LDS, 1 WG/CU:
+//   SKINNY  32x128, 4 wavefronts (1x4, 32x32 each),  40 KiB LDS, 4 WG/CU:
 //           few rows of X against a long stream of W rows (the small-M,
 //           weight-streaming regime, where HBM rather than MFMA bounds);
-//           64-deep K steps through registers, which streamed W faster
-//           here than the direct-to-LDS form
+//           small workgroups so that two or more share a CU and keep enough
+//           weight bytes in flight
 using CfgLarge = TileCfg<256, 256, 32, 4, 2, 1>;
 using CfgMid = TileCfg<128, 256, 32, 2, 4, 1>;
 using CfgSmall = TileCfg<128, 128, 32, 2, 2, 2>;
 using CfgTiny = TileCfg<64, 64, 32, 2, 2, 4>;
-using CfgSkinny = TileCfg<32, 256, 64, 1, 8, 1, false>;  // plain loads stream W faster here
+using CfgSkinny = TileCfg<32, 128, 32, 1, 4, 4>;
 
 enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_COUNT = 5 };
 
@@ -65,7 +65,8 @@ constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at
 constexpr double kRoundFixedS = 5e-6;           // per round of workgroups: first loads, epilogue, drain
 constexpr double kPassFixedS = 2e-6;            // one more kernel on the stream
 constexpr double kPassBytesPerS = 4e12;         // sustained HBM rate of the second passes
-constexpr double kGemmBytesPerS = 5.6e12;       // sustained HBM rate of a weight-streaming GEMM
+constexpr double kGemmBytesPerS = 6.2e12;       // sustained HBM rate of a weight-streaming GEMM
+constexpr double kSingleStreamRate = 0.7;       // fraction of it with fewer than 2 workgroups per CU
 
 struct PendingTiming {
     int role;
@@ -221,7 +222,8 @@ struct Plan {
 //   ceil(steps / S) K steps; the busiest CU runs load = ceil(units / CUs) of
 //   them, w = WG_PER_CU at a time, sharing its matrix pipes, so
 //     t_gemm = ceil(load / w) * t_round + load * 2*BM*BN*k_slice / (peak * eff)
-//   (but never less than the time to stream W and X from HBM once), and a
+//   (but never less than the time to stream W and X from HBM once, 1/0.7
+//   times longer when fewer than two workgroups per CU stream), and a
 //   second pass (split-K or row-max finalize) costs
 //     t_pass = t_launch + (S + 1) * M * N * 4 bytes / HBM rate   (S > 1)
 //            = t_launch                                          (S = 1, row max)
@@ -253,8 +255,11 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
             const double wg_flops = 2.0 * ci.bm * ci.bn * (double)kslice;
             double t = (double)((load + ci.wgs_per_cu - 1) / ci.wgs_per_cu) * kRoundFixedS +
                        (double)load * wg_flops / (kCuPeakFlops * ci.efficiency);
-            // every byte of W (and of X) crosses HBM at least once
-            t = std::max(t, 4.0 * ((double)N * K + (double)M * K) / kGemmBytesPerS);
+            // every byte of W (and of X) crosses HBM at least once, at the
+            // full rate only with two or more workgroups per CU streaming
+            double t_hbm = 4.0 * ((double)N * K + (double)M * K) / kGemmBytesPerS;
+            if (units < 2 * (int64_t)num_cus) t_hbm /= kSingleStreamRate;
+            t = std::max(t, t_hbm);
             if (S > 1)
                 t += kPassFixedS + (S + 1) * (double)M * (double)N * 4.0 / kPassBytesPerS;
             else if (rowmax)

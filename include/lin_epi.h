@@ -151,7 +151,7 @@ enum {
     LIN_EPI_OPT_UNFUSED = 3,
     /* Tile configuration: 0 = automatic (default); 1 = 256x256 tiles with 8
      * wavefronts, 2 = 128x256 with 8, 3 = 128x128 with 4, 4 = 64x64 with 4,
-     * 5 = 32x256 with 8 (few rows, weight streaming).
+     * 5 = 32x128 with 4 (few rows, weight streaming).
      * The split-K choice is still made (or forced) as usual. */
     LIN_EPI_OPT_TILE = 4,
     /* 1 = stage X and W tiles through registers (128-bit loads, then LDS

@@ -278,11 +278,11 @@ def test_every_tile_config_all_tails(tile, tail):
 
 
 @pytest.mark.parametrize("split", [1, 3])
-@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("tile", sorted(lib.TILE_CONFIGS))
 @pytest.mark.parametrize("tail", ALL_TAILS, ids=lambda t: t.name)
 def test_direct_to_lds_equals_register_staging(tile, split, tail):
-    """The 32-deep-K tiles stage operands with direct-to-LDS buffer loads into
-    a swizzled layout by default; forced register staging (padded rows) must
+    """Every tile stages operands with direct-to-LDS buffer loads into a
+    swizzled layout by default; forced register staging (padded rows) must
     give bit-identical results on random inputs, ragged in M, N and K, since
     both feed the same MFMA sequence.  Also checked against the oracle."""
     M, N, K = 261, 530, 1000
