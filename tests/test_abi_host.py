@@ -192,6 +192,11 @@ def test_planner_choices_for_the_workloads(handle):
     assert _plan(handle, 1000, 6000, 4100, A)[:5] == (128, 128, 2, 2, 752)
     # pooled-weight tail (b): a 1024x512x8192 GEMM is split into 8 K slices to fill the device
     assert _plan(handle, 1024, 512, 8192, F)[:4] == (128, 128, 8, 2)
+    # few rows against a long weight stream: 32x128 tiles, split so that two
+    # workgroups per compute unit stream W (512 workgroups)
+    assert _plan(handle, 16, 32768, 32768, C)[:5] == (32, 128, 2, 2, 512)
+    assert _plan(handle, 1, 32768, 32768, C)[:5] == (32, 128, 2, 2, 512)
+    assert _plan(handle, 16, 8192, 8192, C)[:5] == (32, 128, 8, 2, 512)
     # tail (b) unsplit keeps per-tile row maxima: M * tiles_n floats
     t = _plan(handle, 1024, 8192, 8192, B)
     if t[2] == 1:
