@@ -112,6 +112,10 @@ struct TileCfg {
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int DMA_BLOCKS = ((BM + BN) / 8 + NW - 1) / NW * NW;
     static constexpr int LDS_BYTES = DMA ? STAGES * DMA_BLOCKS * 1024 : 2 * (BM + BN) * (BK + 4) * 4;
+    // The register-staged form (padded rows) may fit fewer workgroups per CU.
+    static constexpr int LDS_BYTES_REG = 2 * (BM + BN) * (BK + 4) * 4;
+    static constexpr int WG_PER_CU_REG = WG_PER_CU < 160 * 1024 / LDS_BYTES_REG ? WG_PER_CU : 160 * 1024 / LDS_BYTES_REG;
+    static constexpr int WAVES_PER_SIMD_REG = (WG_PER_CU_REG * WAVES_M * WAVES_N + 3) / 4;
 };
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt
@@ -131,7 +135,7 @@ __device__ __forceinline__ void wait_vmcnt()
 constexpr int64_t kBufferWindow = 1 << 30;
 
 template <class Cfg, int EPI, bool BUF>
-__global__ void __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD)
+__global__ void __launch_bounds__(Cfg::THREADS, BUF ? Cfg::WAVES_PER_SIMD : Cfg::WAVES_PER_SIMD_REG)
 gemm_epi_kernel(GemmArgs a)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WAVES_M = Cfg::WAVES_M, WAVES_N = Cfg::WAVES_N;
