@@ -198,6 +198,14 @@ def _check(rc: int, where: str) -> None:
         raise LinEpiError(rc, where)
 
 
+def _check_tensors(**tensors) -> None:
+    import torch
+
+    for name, t in tensors.items():
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous float32 device tensor" % name)
+
+
 class LinEpi:
     """A handle bound to a torch CUDA (HIP) stream; runs on torch tensors.
 
@@ -252,7 +260,10 @@ class LinEpi:
         """Tail (a)'s scale folded into new weight and bias tensors."""
         import torch
 
+        _check_tensors(W=W, b=b)
         N, K = W.shape
+        if tuple(b.shape) != (N,):
+            raise ValueError("shape mismatch: W %s, b %s" % (tuple(W.shape), tuple(b.shape)))
         Ws = torch.empty_like(W)
         bs = torch.empty_like(b)
         rc = lin_epi_scale_weights(self.handle, N, K, W.data_ptr(), b.data_ptr(), scale, Ws.data_ptr(), bs.data_ptr())
@@ -263,7 +274,12 @@ class LinEpi:
         """Window-averaged weights and bias (device tensors) for tail (b)."""
         import torch
 
+        _check_tensors(W=W, b=b)
         N, K = W.shape
+        if tuple(b.shape) != (N,):
+            raise ValueError("shape mismatch: W %s, b %s" % (tuple(W.shape), tuple(b.shape)))
+        if pool_kernel <= 0:
+            raise ValueError("pool_kernel must be positive")
         L = N // pool_kernel
         Wp = torch.empty((L, K), dtype=torch.float32, device=W.device)
         bp = torch.empty((L,), dtype=torch.float32, device=W.device)
@@ -273,6 +289,10 @@ class LinEpi:
         return Wp, bp
 
     def run_into(self, X, W, b, desc: lin_epi_desc, Y) -> None:
+        """lin_epi_run into a caller-allocated Y.  The fast path for repeated
+        calls: beyond what the C ABI validates (sizes, alignment, kind) the
+        caller guarantees contiguous float32 device tensors X [M,K], W [N,K],
+        b [N] and Y of ``output_shape(M, N, kind)``; :meth:`run` checks them."""
         M, K = X.shape
         N = W.shape[0]
         rc = lin_epi_run(self.handle, M, N, K, X.data_ptr(), W.data_ptr(), b.data_ptr(), desc, Y.data_ptr())
@@ -281,9 +301,7 @@ class LinEpi:
     def run(self, X, W, b, desc: lin_epi_desc):
         import torch
 
-        for name, t in (("X", X), ("W", W), ("b", b)):
-            if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
-                raise ValueError("%s must be a contiguous float32 device tensor" % name)
+        _check_tensors(X=X, W=W, b=b)
         M, K = X.shape
         N, K2 = W.shape
         if K2 != K or tuple(b.shape) != (N,):
