@@ -21,7 +21,11 @@ What it computes, in the pages' order and unfused:
   analysis (swish, then scaling).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against brute
-force, closed forms, invariants and the worked example of page l2_p98.
+force, closed forms, invariants and the worked example of page l2_p98,
+including the dispatch ``apply_tail``/``forward_rows`` for every kind (kind 4
+by page l2_p98's fold identity: it must equal tail (b) of the unpooled layer),
+and ``tests/test_oracle_mutants.py`` checks that the pins reject mistakes
+planted in ``oracle.c`` and in this file.
 """
 
 from __future__ import annotations

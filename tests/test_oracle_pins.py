@@ -300,3 +300,96 @@ def test_checked_rows():
     assert r.size == 64 and r[0] == 0 and r[-1] == 2047 and np.unique(r).size == 64
     assert np.array_equal(r, workloads.checked_rows(2048))
     assert np.array_equal(workloads.checked_rows(40), np.arange(40))
+
+
+# --------------------------------------------------------------------------
+# Dispatch: forward_rows / apply_tail, the route every GPU parity test takes.
+# Each kind is pinned through that route, so a mistake in the dispatch itself
+# (arguments swapped or dropped, the wrong window) fails here too.
+# --------------------------------------------------------------------------
+
+def _column_layer(values):
+    """X = I_K, W = values as one output feature, b = 0: the linear output of
+    row m is values[m] exactly, so forward_rows exposes the tail alone."""
+    v = np.asarray(values, dtype=np.float32)
+    X = np.eye(v.size, dtype=np.float32)
+    return X, v[None, :].copy(), np.zeros(1, dtype=np.float32)
+
+
+def test_dispatch_kind0_is_the_linear_layer():
+    K, N = 24, 37
+    _, W, b = workloads.make_inputs(1, N, K, seed=14)
+    X = np.eye(K, dtype=np.float32)
+    y = oracle.forward_rows(X, W, b, oracle.KIND_NONE, scale=3.0, lo=-0.5, hi=0.5)
+    assert np.array_equal(y, W.T.astype(np.float64) + b.astype(np.float64))
+    rows = np.array([5, 0, 23])
+    assert np.array_equal(oracle.forward_rows(X, W, b, oracle.KIND_NONE, rows), y[rows])
+
+
+def test_dispatch_kind1_op_order_and_saturation():
+    """The points of the tail (a) closed-form pin, run through forward_rows."""
+    X, W, b = _column_layer([0.0, 3.0, -3.0, 4.0, 5.0, -4.0, -100.0, 100.0, 1.0])
+    out = oracle.forward_rows(X, W, b, oracle.KIND_SCALE_HARDTANH_GELU, scale=0.5, lo=-2.0, hi=2.0)[:, 0]
+    phi2 = 0.9772498680518208
+    assert out[0] == 0.0
+    assert abs(out[1] - 1.5 * stats.norm.cdf(1.5)) < 1e-14     # scale before the clamp
+    assert abs(out[2] - (-1.5) * stats.norm.cdf(-1.5)) < 1e-14
+    for i in (3, 4, 7):
+        assert abs(out[i] - 2.0 * phi2) < 1e-14                # saturates at GELU(2)
+    for i in (5, 6):
+        assert abs(out[i] - (-2.0) * (1 - phi2)) < 1e-14       # and at GELU(-2)
+    assert abs(out[8] - 0.5 * stats.norm.cdf(0.5)) < 1e-14
+
+
+def test_dispatch_kind1_asymmetric_clamp():
+    """lo and hi reach the clamp in that order: [-1, 3] with scale 2."""
+    X, W, b = _column_layer([1.0, -1.0, 2.0])
+    out = oracle.forward_rows(X, W, b, oracle.KIND_SCALE_HARDTANH_GELU, scale=2.0, lo=-1.0, hi=3.0)[:, 0]
+    np.testing.assert_allclose(out, [2 * stats.norm.cdf(2), -stats.norm.cdf(-1), 3 * stats.norm.cdf(3)], atol=1e-14)
+
+
+def test_dispatch_kind2_worked_example_window():
+    """The page's worked example (window 2) through forward_rows: the row max
+    of 2*GELU over the pooled values [1.5, 4.5]."""
+    g = _golden("pool_fold_worked_example.json")
+    X = np.array(g["x"], dtype=np.float32)
+    W = np.array(g["W"], dtype=np.float32)
+    b = np.array(g["b"], dtype=np.float32)
+    out = oracle.forward_rows(X, W, b, oracle.KIND_POOL_GELU_SCALE_ROWMAX, scale=2.0, pool_kernel=g["pool_kernel"])
+    p = np.array(g["pooled"][0])
+    assert abs(out[0] - (2.0 * p * stats.norm.cdf(p)).max()) < 1e-14
+
+
+def _window_mean_rows(a, k):
+    """Mean of each run of k consecutive rows (exact here: dyadic data)."""
+    a = np.asarray(a, dtype=np.float64)
+    L = a.shape[0] // k
+    return a[: L * k].reshape((L, k) + a.shape[1:]).mean(axis=1)
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(6, 64, 20, 15), (9, 16 * 7 + 5, 12, 16)])
+def test_dispatch_kind4_fold_identity(M, N, K, seed):
+    """Page l2_p98's fold identity: tail (b) of the layer equals kind 4 (no
+    pooling) on the layer with window-averaged weights and bias.  Integer
+    inputs make both linear outputs exact, so the two sides agree to 1e-12."""
+    X, W, b = workloads.integer_inputs(M, N, K, seed=seed)
+    Wp = _window_mean_rows(W, 16).astype(np.float32)
+    bp = _window_mean_rows(b, 16).astype(np.float32)
+    assert np.array_equal(Wp.astype(np.float64), _window_mean_rows(W, 16))  # exact in fp32
+    direct = oracle.apply_tail(oracle.linear_rows(X, W, b), oracle.KIND_POOL_GELU_SCALE_ROWMAX, 2.0)
+    folded = oracle.apply_tail(oracle.linear_rows(X, Wp, bp), oracle.KIND_GELU_SCALE_ROWMAX, 2.0)
+    assert folded.shape == (M,)
+    np.testing.assert_allclose(folded, direct, rtol=0, atol=1e-12)
+    via_rows = oracle.forward_rows(X, Wp, bp, oracle.KIND_GELU_SCALE_ROWMAX, scale=2.0)
+    assert np.array_equal(via_rows, folded)
+
+
+def test_dispatch_kind4_is_rowmax_of_scaled_gelu():
+    # one row, three output features with linear outputs -0.75, 0.25, -3
+    Xr = np.ones((1, 1), dtype=np.float32)
+    Wr = np.array([[-0.75], [0.25], [-3.0]], dtype=np.float32)
+    br = np.zeros(3, dtype=np.float32)
+    out = oracle.forward_rows(Xr, Wr, br, oracle.KIND_GELU_SCALE_ROWMAX, scale=2.0)
+    v = np.array([-0.75, 0.25, -3.0])
+    assert out.shape == (1,)
+    assert abs(out[0] - (2.0 * v * stats.norm.cdf(v)).max()) < 1e-14
