@@ -36,6 +36,7 @@ LIN_EPI_OPT_PROFILE = 2
 LIN_EPI_OPT_UNFUSED = 3
 LIN_EPI_OPT_TILE = 4
 LIN_EPI_OPT_REG_STAGING = 5
+LIN_EPI_OPT_GRID = 6
 TILE_CONFIGS = {1: (256, 256), 2: (128, 256), 3: (128, 128), 4: (64, 64), 5: (32, 128)}
 
 # every function include/lin_epi.h declares
@@ -73,6 +74,7 @@ class lin_epi_plan(ctypes.Structure):
         ("grid_main", ctypes.c_int64),
         ("kernels", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64),
+        ("schedule", ctypes.c_int32),
     ]
 
 
@@ -210,7 +212,13 @@ class LinEpi:
     """A handle bound to a torch CUDA (HIP) stream; runs on torch tensors.
 
     ``run(X, W, b, desc)`` allocates Y with torch (device memory only) and
-    calls lin_epi_run; the result is enqueued on the handle's stream.
+    calls lin_epi_run; the result is enqueued on the handle's stream.  Tensors
+    the handle allocates come from torch's caching allocator on that stream,
+    and input tensors are marked as used on it (``record_stream``) when the
+    caller's current stream is another one, so the allocator does not hand
+    their memory to other work before the handle's stream has finished with
+    it.  A caller reading Y on another stream synchronises with the handle's
+    stream first.
     """
 
     def __init__(self, stream=None):
@@ -218,6 +226,26 @@ class LinEpi:
         ptr = stream.cuda_stream if stream is not None else 0
         rc, self.handle = lin_epi_create(ptr)
         _check(rc, "lin_epi_create")
+
+    def _torch_stream(self, device):
+        import torch
+
+        return self.stream if self.stream is not None else torch.cuda.default_stream(device)
+
+    def _alloc(self, shape, device):
+        """An uninitialised float32 tensor owned by the handle's stream."""
+        import torch
+
+        with torch.cuda.stream(self._torch_stream(device)):
+            return torch.empty(shape, dtype=torch.float32, device=device)
+
+    def _mark_used(self, *tensors) -> None:
+        import torch
+
+        s = self._torch_stream(tensors[0].device)
+        if torch.cuda.current_stream(tensors[0].device) != s:
+            for t in tensors:
+                t.record_stream(s)
 
     def close(self) -> None:
         if self.handle:
@@ -258,22 +286,19 @@ class LinEpi:
 
     def scale_weights(self, W, b, scale: float):
         """Tail (a)'s scale folded into new weight and bias tensors."""
-        import torch
-
         _check_tensors(W=W, b=b)
         N, K = W.shape
         if tuple(b.shape) != (N,):
             raise ValueError("shape mismatch: W %s, b %s" % (tuple(W.shape), tuple(b.shape)))
-        Ws = torch.empty_like(W)
-        bs = torch.empty_like(b)
+        Ws = self._alloc((N, K), W.device)
+        bs = self._alloc((N,), W.device)
         rc = lin_epi_scale_weights(self.handle, N, K, W.data_ptr(), b.data_ptr(), scale, Ws.data_ptr(), bs.data_ptr())
         _check(rc, "lin_epi_scale_weights")
+        self._mark_used(W, b)
         return Ws, bs
 
     def pool_weights(self, W, b, pool_kernel: int = 16):
         """Window-averaged weights and bias (device tensors) for tail (b)."""
-        import torch
-
         _check_tensors(W=W, b=b)
         N, K = W.shape
         if tuple(b.shape) != (N,):
@@ -281,11 +306,12 @@ class LinEpi:
         if pool_kernel <= 0:
             raise ValueError("pool_kernel must be positive")
         L = N // pool_kernel
-        Wp = torch.empty((L, K), dtype=torch.float32, device=W.device)
-        bp = torch.empty((L,), dtype=torch.float32, device=W.device)
+        Wp = self._alloc((L, K), W.device)
+        bp = self._alloc((L,), W.device)
         rc = lin_epi_pool_weights(self.handle, N, K, W.data_ptr(), b.data_ptr(), pool_kernel, Wp.data_ptr(),
                                   bp.data_ptr())
         _check(rc, "lin_epi_pool_weights")
+        self._mark_used(W, b)
         return Wp, bp
 
     def run_into(self, X, W, b, desc: lin_epi_desc, Y) -> None:
@@ -299,13 +325,12 @@ class LinEpi:
         _check(rc, "lin_epi_run")
 
     def run(self, X, W, b, desc: lin_epi_desc):
-        import torch
-
         _check_tensors(X=X, W=W, b=b)
         M, K = X.shape
         N, K2 = W.shape
         if K2 != K or tuple(b.shape) != (N,):
             raise ValueError("shape mismatch: X %s, W %s, b %s" % (tuple(X.shape), tuple(W.shape), tuple(b.shape)))
-        Y = torch.empty(self.output_shape(M, N, desc.kind), dtype=torch.float32, device=X.device)
+        Y = self._alloc(self.output_shape(M, N, desc.kind), X.device)
         self.run_into(X, W, b, desc, Y)
+        self._mark_used(X, W, b)
         return Y

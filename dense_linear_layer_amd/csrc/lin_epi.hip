@@ -57,16 +57,16 @@ static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
               "LDS budget");
 
 // Time-model constants of the planner, fitted (with the efficiencies above)
-// to 177 timed (shape, tail, configuration, split) combinations over 15
-// problems on MI355X, each timed after 60 ms of warm-up so the engine clock
-// has ramped up; the chosen plan is the measured best for 10 of them and
-// within 6 % for the rest (all under 1 % but two problems under 0.1 ms).
+// to timed (shape, tail, configuration, grid) combinations on MI355X, each
+// timed after enough warm-up for the engine clock to have ramped up.
 constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at the 2.4 GHz peak clock
 constexpr double kRoundFixedS = 5e-6;           // per round of workgroups: first loads, epilogue, drain
 constexpr double kPassFixedS = 2e-6;            // one more kernel on the stream
-constexpr double kPassBytesPerS = 4e12;         // sustained HBM rate of the second passes
+constexpr double kPassBytesPerS = 4e12;         // sustained HBM rate of partial-sum traffic
 constexpr double kGemmBytesPerS = 6.2e12;       // sustained HBM rate of a weight-streaming GEMM
 constexpr double kSingleStreamRate = 0.7;       // fraction of it with fewer than 2 workgroups per CU
+constexpr double kFixupFixedS = 3e-6;           // split tiles: release/acquire and the finishing reads
+constexpr double kCuBytesPerS = 60e9;           // one workgroup reading other segments' sums
 
 struct PendingTiming {
     int role;
@@ -81,7 +81,9 @@ struct lin_epi_ctx {
     int num_cus = 0;
     void *ws = nullptr;
     size_t ws_bytes = 0;
+    size_t ws_clean = 0;  // leading workspace bytes known to be zero between runs (the arrival counters)
     int64_t split_opt = 0;
+    int64_t grid_opt = 0;
     int64_t tile_opt = 0;
     bool profile = false;
     bool unfused = false;
@@ -116,6 +118,7 @@ int ensure_workspace(lin_epi_ctx *h, size_t bytes)
         (void)hipFree(h->ws);
         h->ws = nullptr;
         h->ws_bytes = 0;
+        h->ws_clean = 0;
     }
     const size_t rounded = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
     if (hipMalloc(&h->ws, rounded) != hipSuccess) {
@@ -124,6 +127,7 @@ int ensure_workspace(lin_epi_ctx *h, size_t bytes)
         return LIN_EPI_ENOMEM;
     }
     h->ws_bytes = rounded;
+    h->ws_clean = 0;
     return LIN_EPI_OK;
 }
 
@@ -171,116 +175,38 @@ int timed_launch(lin_epi_ctx *h, int role, Launch &&launch)
 
 // reg_staging: stage operands through registers even where the buffer-load
 // (direct-to-LDS) path is usable (LIN_EPI_OPT_REG_STAGING).
-template <class Cfg, int EPI>
-void launch_gemm_cfg(const GemmArgs &g, int64_t grid_x, int split, hipStream_t s, bool reg_staging)
+template <class Cfg, int EPI, bool SPLIT>
+void launch_gemm_cfg(const GemmArgs &g, int64_t grid, hipStream_t s, bool reg_staging)
 {
-    const dim3 grid((unsigned)grid_x, (unsigned)split), block(Cfg::THREADS);
+    const dim3 gr((unsigned)grid), block(Cfg::THREADS);
     if constexpr (Cfg::BUFLOAD) {
         // buffer loads while a tile's rows of X and W span less than the window
         if (!reg_staging && (int64_t)std::max(Cfg::BM, Cfg::BN) * g.K * 4 < kBufferWindow) {
-            hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI, true>), grid, block, 0, s, g);
+            hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI, true, SPLIT>), gr, block, 0, s, g);
             return;
         }
     }
-    hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_epi_kernel<Cfg, EPI, false, SPLIT>), gr, block, 0, s, g);
 }
 
+// multi: the grid is not one workgroup per tile, so workgroups walk ranges
+// of (tile, K step) iterations (the kernels with the segment loop and the
+// partial-sum code)
 template <int EPI>
-void launch_gemm(int cfg, const GemmArgs &g, int64_t grid_x, int split, hipStream_t s, bool reg_staging)
+void launch_gemm(int cfg, bool multi, const GemmArgs &g, int64_t grid, hipStream_t s, bool reg_staging)
 {
-    switch (cfg) {
-        case CFG_LARGE: launch_gemm_cfg<CfgLarge, EPI>(g, grid_x, split, s, reg_staging); break;
-        case CFG_MID: launch_gemm_cfg<CfgMid, EPI>(g, grid_x, split, s, reg_staging); break;
-        case CFG_SMALL: launch_gemm_cfg<CfgSmall, EPI>(g, grid_x, split, s, reg_staging); break;
-        case CFG_TINY: launch_gemm_cfg<CfgTiny, EPI>(g, grid_x, split, s, reg_staging); break;
-        default: launch_gemm_cfg<CfgSkinny, EPI>(g, grid_x, split, s, reg_staging); break;
+    switch (cfg * 2 + (multi ? 1 : 0)) {
+        case CFG_LARGE * 2: launch_gemm_cfg<CfgLarge, EPI, false>(g, grid, s, reg_staging); break;
+        case CFG_LARGE * 2 + 1: launch_gemm_cfg<CfgLarge, EPI, true>(g, grid, s, reg_staging); break;
+        case CFG_MID * 2: launch_gemm_cfg<CfgMid, EPI, false>(g, grid, s, reg_staging); break;
+        case CFG_MID * 2 + 1: launch_gemm_cfg<CfgMid, EPI, true>(g, grid, s, reg_staging); break;
+        case CFG_SMALL * 2: launch_gemm_cfg<CfgSmall, EPI, false>(g, grid, s, reg_staging); break;
+        case CFG_SMALL * 2 + 1: launch_gemm_cfg<CfgSmall, EPI, true>(g, grid, s, reg_staging); break;
+        case CFG_TINY * 2: launch_gemm_cfg<CfgTiny, EPI, false>(g, grid, s, reg_staging); break;
+        case CFG_TINY * 2 + 1: launch_gemm_cfg<CfgTiny, EPI, true>(g, grid, s, reg_staging); break;
+        case CFG_SKINNY * 2: launch_gemm_cfg<CfgSkinny, EPI, false>(g, grid, s, reg_staging); break;
+        default: launch_gemm_cfg<CfgSkinny, EPI, true>(g, grid, s, reg_staging); break;
     }
-}
-
-template <int EPI>
-void launch_reduce(const float *P, const float *bias, float *Y, int64_t MN, int N, int S, TailParams t,
-                   hipStream_t s)
-{
-    const int32_t vec4 = (N % 4 == 0) && (((uintptr_t)Y & 15u) == 0) && (((uintptr_t)P & 15u) == 0);
-    int64_t blocks = ((vec4 ? MN / 4 : MN) + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, s, P, bias, Y, MN, N, S, t,
-                       vec4);
-}
-
-struct Plan {
-    int cfg;
-    int split;
-    int64_t k_slice;
-    int tiles_m, tiles_n;
-};
-
-// Pick the tile configuration and the number of K slices by estimated time.
-// For each configuration and slice count S (1..16, at most one per K step):
-//   units = tiles * S workgroups, each computing a BM x BN tile over
-//   ceil(steps / S) K steps; the busiest CU runs load = ceil(units / CUs) of
-//   them, w = WG_PER_CU at a time, sharing its matrix pipes, so
-//     t_gemm = ceil(load / w) * t_round + load * 2*BM*BN*k_slice / (peak * eff)
-//   (but never less than the time to stream W and X from HBM once, 1/0.7
-//   times longer when fewer than two workgroups per CU stream), and a
-//   second pass (split-K or row-max finalize) costs
-//     t_pass = t_launch + (S + 1) * M * N * 4 bytes / HBM rate   (S > 1)
-//            = t_launch                                          (S = 1, row max)
-// Padding waste is included (a tile's work counts in full).  The fastest
-// estimate wins; LIN_EPI_OPT_SPLIT_K = 1 forbids a split and S >= 2 forces
-// one (clamped to the K steps available, so every slice owns at least one).
-// For the row-max tails a split moves pooling, GELU and the max into the
-// second pass, which reads complete sums.
-Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind, int num_cus)
-{
-    Plan best{CFG_SMALL, 1, 0, 0, 0};
-    double best_t = 1e300;
-    // (every configuration that is not excluded by the override scores at
-    // least S = 1, so `best` is always set)
-    const bool rowmax = kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX || kind == LIN_EPI_GELU_SCALE_ROWMAX;
-    for (int c = 0; c < CFG_COUNT; ++c) {
-        const CfgInfo &ci = kCfgs[c];
-        const int64_t tm = (M + ci.bm - 1) / ci.bm, tn = (N + ci.bn - 1) / ci.bn;
-        const int64_t tiles = tm * tn;
-        const int64_t steps = (K + ci.bk - 1) / ci.bk;
-        if (h->tile_opt > 0 && c != h->tile_opt - 1) continue;
-        int s_lo = 1, s_hi = (int)std::min<int64_t>(16, std::max<int64_t>(steps, 1));
-        if (h->split_opt == 1) s_hi = 1;
-        if (h->split_opt >= 2) s_lo = s_hi = (int)std::min<int64_t>(h->split_opt, std::max<int64_t>(steps, 1));
-        for (int S = s_lo; S <= s_hi; ++S) {
-            const int64_t units = tiles * S;
-            const int64_t load = (units + num_cus - 1) / num_cus;
-            const int64_t kslice = ((steps + S - 1) / S) * ci.bk;
-            const double wg_flops = 2.0 * ci.bm * ci.bn * (double)kslice;
-            double t = (double)((load + ci.wgs_per_cu - 1) / ci.wgs_per_cu) * kRoundFixedS +
-                       (double)load * wg_flops / (kCuPeakFlops * ci.efficiency);
-            // every byte of W (and of X) crosses HBM at least once, at the
-            // full rate only with two or more workgroups per CU streaming
-            double t_hbm = 4.0 * ((double)N * K + (double)M * K) / kGemmBytesPerS;
-            if (units < 2 * (int64_t)num_cus) t_hbm /= kSingleStreamRate;
-            t = std::max(t, t_hbm);
-            if (S > 1)
-                t += kPassFixedS + (S + 1) * (double)M * (double)N * 4.0 / kPassBytesPerS;
-            else if (rowmax)
-                t += kPassFixedS;
-            if (t < best_t) {
-                best_t = t;
-                best = Plan{c, S, 0, (int)tm, (int)tn};
-            }
-        }
-    }
-    const CfgInfo &ci = kCfgs[best.cfg];
-    const int64_t steps = (K + ci.bk - 1) / ci.bk;
-    if (best.split > 1 && steps > 0) {
-        best.k_slice = (steps + best.split - 1) / best.split * ci.bk;
-        best.split = (int)((K + best.k_slice - 1) / best.k_slice);
-    }
-    if (best.split <= 1) {
-        best.split = 1;
-        best.k_slice = steps > 0 ? steps * ci.bk : ci.bk;
-    }
-    return best;
 }
 
 bool is_rowmax(int kind)
@@ -288,38 +214,168 @@ bool is_rowmax(int kind)
     return kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX || kind == LIN_EPI_GELU_SCALE_ROWMAX;
 }
 
-// The launch plan of one lin_epi_run call: tile configuration and K slices
-// from choose_plan, then the kernels the chosen path launches and the
-// workspace it needs.
-//   fused, no split:       GEMM+tail (1 kernel); row-max kinds add the
-//                          finalize pass and M*tiles_n partial maxima
-//   fused, split S:        GEMM partials [S,M,N] + second pass (2 kernels)
-//   unfused ablation:      GEMM (+ reduce if split) to raw y, then a tail
-//                          kernel (none for kind 0); raw y for the row-max
-//                          kinds lives in the workspace after the partials
+// Shape of the work partition for a grid of G workgroups over T = tiles *
+// steps iterations (schedule.hpp): how many K segments the tiles are cut
+// into in all, and at most per tile.
+struct SegStats {
+    int64_t segments;  // sum over tiles of their segment counts
+    int max_per_tile;
+};
+
+SegStats seg_stats(int64_t tiles, int steps, int64_t G)
+{
+    if (G == tiles) return SegStats{tiles, 1};
+    if (G % tiles == 0) return SegStats{G, (int)(G / tiles)};  // split-K: S segments per tile
+    // stream-K: a range boundary strictly inside a tile adds a segment
+    const int64_t T = tiles * steps;
+    const Partition p{steps, (int)G, 0, (int)(T / G), (int)(T % G)};
+    SegStats st{tiles, 1};
+    int64_t prev_t = -1;
+    int run = 1;
+    for (int v = 1; v < (int)G; ++v) {
+        const int64_t b = range_begin(p, v);
+        if (b % steps == 0) continue;
+        ++st.segments;
+        const int64_t t = b / steps;
+        run = t == prev_t ? run + 1 : 2;
+        prev_t = t;
+        if (run > st.max_per_tile) st.max_per_tile = run;
+    }
+    return st;
+}
+
+struct Plan {
+    int cfg;
+    int64_t grid;  // workgroups of the GEMM kernel
+    int schedule;  // 0 one tile per workgroup, 1 split-K, 2 stream-K
+    int max_seg;   // largest number of K segments of one tile
+    int64_t segments;
+    int tiles_m, tiles_n;
+    int steps;
+};
+
+// Pick the tile configuration and the grid by estimated time.  For each
+// configuration the candidate grids are one tile per workgroup, split-K
+// with S = 2..16 equal K segments per tile (at most one per K step), and
+// stream-K with one or two workgroups per matrix-core slot; then
+//   busiest CU: load = ceil(G / CUs) workgroups of ceil(T / G) K steps,
+//   w = WG_PER_CU of them at a time sharing its matrix pipes:
+//     t_gemm = ceil(load / w) * t_round + load * n_it * 2*BM*BN*32 / (peak * eff)
+//   (never less than the time to stream W and X from HBM once, 1/0.7 times
+//   longer when fewer than two workgroups per CU stream); split tiles add
+//     t_fix = t_fix0 + (published sums, written and read) / HBM rate
+//           + (max segments - 1) * slot / one workgroup's read rate
+//   and the row-max tails one finalize kernel.
+// Padding waste is included (a tile's work counts in full).  The fastest
+// estimate wins.  LIN_EPI_OPT_SPLIT_K = 1 forbids splitting, S >= 2 forces
+// S segments per tile (clamped to the K steps available);
+// LIN_EPI_OPT_GRID = G forces a grid of G workgroups (clamped to T).
+Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind, int num_cus)
+{
+    Plan best{CFG_SMALL, 1, 0, 1, 1, 1, 1, 1};
+    double best_t = 1e300;
+    const bool rowmax = is_rowmax(kind);
+    const int steps = k_steps((int)K);
+    for (int c = 0; c < CFG_COUNT; ++c) {
+        const CfgInfo &ci = kCfgs[c];
+        if (h->tile_opt > 0 && c != h->tile_opt - 1) continue;
+        const int64_t tm = (M + ci.bm - 1) / ci.bm, tn = (N + ci.bn - 1) / ci.bn;
+        const int64_t tiles = tm * tn;
+        const int64_t T = tiles * steps;
+        const int64_t slots = num_cus * (int64_t)ci.wgs_per_cu;
+        std::vector<int64_t> grids;
+        if (h->grid_opt > 0) {
+            grids.push_back(std::min<int64_t>(h->grid_opt, T));
+        } else if (h->split_opt == 1) {
+            grids.push_back(tiles);
+        } else if (h->split_opt >= 2) {
+            grids.push_back(tiles * std::min<int64_t>(h->split_opt, steps));
+        } else {
+            for (int S = 1; S <= std::min(16, steps); ++S) grids.push_back(tiles * S);
+            for (int64_t g : {slots, 2 * slots})
+                if (g > tiles && g < T && g % tiles != 0) grids.push_back(g);
+        }
+        const double slot_bytes = 4.0 * ci.bm * ci.bn / (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);
+        // The 256x256 tile's accumulators leave no room for reading back
+        // whole raw partial tiles (that kernel spills), so unless forced it
+        // only splits for tail (b), whose partials are pooled.
+        const bool forced = h->grid_opt > 0 || h->split_opt >= 2;
+        const bool raw_split_ok = c != CFG_LARGE || kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX || forced;
+        for (int64_t G : grids) {
+            // other grids need 32-bit iteration indices (T < 2^31); the
+            // 256x256 tile only splits where it does not spill
+            if (G != tiles && (T > INT32_MAX || G > INT32_MAX || !raw_split_ok)) G = tiles;
+            const int64_t n_it = (T + G - 1) / G;
+            const int64_t load = (G + num_cus - 1) / num_cus;
+            const double step_flops = 2.0 * ci.bm * ci.bn * kStepK;
+            double t = (double)((load + ci.wgs_per_cu - 1) / ci.wgs_per_cu) * kRoundFixedS +
+                       (double)load * n_it * step_flops / (kCuPeakFlops * ci.efficiency);
+            double t_hbm = 4.0 * ((double)N * K + (double)M * K) / kGemmBytesPerS;
+            if (G < 2 * (int64_t)num_cus) t_hbm /= kSingleStreamRate;
+            t = std::max(t, t_hbm);
+            const SegStats st = seg_stats(tiles, steps, G);
+            if (st.segments > tiles)
+                t += kFixupFixedS + 2.0 * (double)(st.segments - tiles) * slot_bytes / kPassBytesPerS +
+                     (st.max_per_tile - 1) * slot_bytes / kCuBytesPerS;
+            if (rowmax) t += kPassFixedS;
+            if (t < best_t) {
+                best_t = t;
+                best = Plan{c, G, G == tiles ? 0 : G % tiles == 0 ? 1 : 2, st.max_per_tile, st.segments,
+                            (int)tm, (int)tn, steps};
+            }
+        }
+    }
+    return best;
+}
+
+// Workspace layout of one run: [arrival counters, one int per tile, rounded
+// up to 256 bytes][partial-sum slots when tiles are split: one per
+// workgroup for split-K, two for stream-K][row-max partials M * tiles_n]
+// [raw linear output M * N: unfused row-max tails only].
+struct WsLayout {
+    size_t counters, partials, rowmax, raw, total;  // byte offsets and size
+};
+
+WsLayout ws_layout(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, int kind)
+{
+    WsLayout w{};
+    const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
+    const bool split = pl.segments > tiles;
+    const int64_t slot = (int64_t)kCfgs[pl.cfg].bm * kCfgs[pl.cfg].bn /
+                         (!h->unfused && kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    w.counters = 0;
+    w.partials = up((size_t)tiles * sizeof(int32_t));
+    const int64_t nslots = pl.schedule == 2 ? 2 * pl.grid : pl.grid;  // split-K never crosses a tile
+    w.rowmax = w.partials + (split ? up((size_t)(nslots * slot) * sizeof(float)) : 0);
+    const bool rm = is_rowmax(kind);
+    w.raw = w.rowmax + (rm && !h->unfused ? up((size_t)(M * pl.tiles_n) * sizeof(float)) : 0);
+    w.total = w.raw + (rm && h->unfused ? up((size_t)(M * N) * sizeof(float)) : 0);
+    return w;
+}
+
+// The launch plan of one lin_epi_run call as the C interface reports it.
+//   fused:    GEMM with the tail in its epilogue (1 kernel); the row-max
+//             kinds add the finalize pass over per-tile row maxima
+//   unfused:  GEMM to raw y (Y itself for the elementwise kinds, the
+//             workspace for the row-max kinds), then a tail kernel (none for
+//             kind 0)
 lin_epi_plan describe(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, int kind)
 {
     lin_epi_plan p{};
     p.tile_m = kCfgs[pl.cfg].bm;
     p.tile_n = kCfgs[pl.cfg].bn;
     p.tile_k = kCfgs[pl.cfg].bk;
-    p.split_k = pl.split;
-    p.grid_main = (int64_t)pl.tiles_m * pl.tiles_n * pl.split;
-    const int64_t MN = M * N;
-    const int64_t partials = pl.split > 1 ? (int64_t)pl.split * MN : 0;
-    if (h->unfused) {
-        p.kernels = (pl.split > 1 ? 2 : 1) + (kind != LIN_EPI_NONE ? 1 : 0);
-        p.workspace_bytes = (partials + (is_rowmax(kind) ? MN : 0)) * (int64_t)sizeof(float);
-    } else if (pl.split > 1) {
-        p.kernels = 2;
-        p.workspace_bytes = partials * (int64_t)sizeof(float);
-    } else if (is_rowmax(kind)) {
-        p.kernels = 2;
-        p.workspace_bytes = M * pl.tiles_n * (int64_t)sizeof(float);
-    } else {
-        p.kernels = 1;
-        p.workspace_bytes = 0;
-    }
+    p.split_k = pl.max_seg;
+    p.grid_main = pl.grid;
+    p.schedule = pl.schedule;
+    if (h->unfused)
+        p.kernels = 1 + (kind != LIN_EPI_NONE ? 1 : 0);
+    else
+        p.kernels = is_rowmax(kind) ? 2 : 1;
+    const WsLayout w = ws_layout(h, pl, M, N, kind);
+    const bool split = pl.segments > (int64_t)pl.tiles_m * pl.tiles_n;
+    p.workspace_bytes = (split || is_rowmax(kind)) ? (int64_t)w.total : 0;
     return p;
 }
 
@@ -392,6 +448,10 @@ int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value)
         case LIN_EPI_OPT_SPLIT_K:
             if (value < 0 || value > 64) return LIN_EPI_EINVAL;
             h->split_opt = value;
+            return LIN_EPI_OK;
+        case LIN_EPI_OPT_GRID:
+            if (value < 0 || value > INT32_MAX) return LIN_EPI_EINVAL;
+            h->grid_opt = value;
             return LIN_EPI_OK;
         case LIN_EPI_OPT_PROFILE:
             if (value != 0 && value != 1) return LIN_EPI_EINVAL;
@@ -466,11 +526,12 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
     const bool rowmax = is_rowmax(kind);
     const bool unfused = h->unfused;
     const Plan pl = choose_plan(h, M, N, K, kind, h->num_cus);
-    const int tiles_m = pl.tiles_m, tiles_n = pl.tiles_n;
-    const int64_t tiles = (int64_t)tiles_m * tiles_n;
-    const int split = pl.split;
-    const int64_t MN = M * N;
-    lin_epi_plan plan = describe(h, pl, M, N, kind);
+    const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
+    const lin_epi_plan plan = describe(h, pl, M, N, kind);
+    const WsLayout wl = ws_layout(h, pl, M, N, kind);
+    const bool split = pl.segments > tiles;  // some tile is cut into K segments
+    const bool multi = pl.grid != tiles;     // workgroups walk ranges (segment-loop kernel)
+    hipStream_t s = h->stream;
 
     GemmArgs g{};
     g.X = X;
@@ -479,113 +540,79 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
     g.M = (int32_t)M;
     g.N = (int32_t)N;
     g.K = (int32_t)K;
-    g.k_slice = (int32_t)pl.k_slice;
-    g.tiles_m = tiles_m;
-    g.tiles_n = tiles_n;
+    g.tiles_m = pl.tiles_m;
+    g.tiles_n = pl.tiles_n;
+    g.steps = pl.steps;
+    g.koff = k_offset((int)K);
+    g.split = pl.schedule == 1 ? (int32_t)(pl.grid / tiles) : 0;
+    g.q = multi ? (int32_t)(tiles * pl.steps / pl.grid) : 0;
+    g.r = multi ? (int32_t)(tiles * pl.steps % pl.grid) : 0;
     g.tail = TailParams{desc->scale, desc->ht_min, desc->ht_max};
 
-    hipStream_t s = h->stream;
-    if (!unfused && rowmax && split > 1) {
-        // Split-K partial sums -> one pass that adds the slices in order,
-        // adds the bias, pools, applies GELU and the scale and takes the max.
-        const size_t bytes = (size_t)split * MN * sizeof(float);
-        rc = ensure_workspace(h, bytes);
+    char *ws = nullptr;
+    if (split || rowmax) {
+        rc = ensure_workspace(h, wl.total);
         if (rc != LIN_EPI_OK) return rc;
-        g.out = static_cast<float *>(h->ws);
-        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s, h->reg_staging); });
-        if (rc != LIN_EPI_OK) return rc;
-        const float *P = static_cast<const float *>(h->ws);
-        const int32_t pool = kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1;
-        const float scale = desc->scale;
-        const int32_t Ni = (int32_t)N;
-        rc = timed_launch(h, 1, [&] {
-            hipLaunchKernelGGL(rowmax_pass_kernel, dim3((unsigned)M), dim3(256), 0, s, P, b, Y, MN, Ni, split, pool,
-                               scale, (int32_t)(N % 4 == 0));
-        });
-        if (rc != LIN_EPI_OK) return rc;
-    } else if (!unfused && rowmax) {
+        ws = static_cast<char *>(h->ws);
+        if (split && wl.partials > h->ws_clean) {
+            // arrival counters start at zero (and every run leaves them so)
+            const int64_t n = (int64_t)(wl.partials / sizeof(int32_t));
+            const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
+            hipLaunchKernelGGL(zero_counters_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<int32_t *>(ws), n);
+            if (hipGetLastError() != hipSuccess) return LIN_EPI_EHIP;
+            h->ws_clean = wl.partials;
+        }
+        g.counters = reinterpret_cast<int32_t *>(ws + wl.counters);
+        g.partials = reinterpret_cast<float *>(ws + wl.partials);
+    }
+
+    if (!unfused && rowmax) {
         // GEMM with the row-max epilogue -> per-(row, column tile) partials ->
-        // deterministic max over column tiles.
-        const size_t bytes = (size_t)M * tiles_n * sizeof(float);
-        rc = ensure_workspace(h, bytes);
-        if (rc != LIN_EPI_OK) return rc;
-        g.out = static_cast<float *>(h->ws);
+        // max over column tiles.
+        g.out = reinterpret_cast<float *>(ws + wl.rowmax);
         rc = timed_launch(h, 0, [&] {
             if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX)
-                launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s, h->reg_staging);
+                launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(pl.cfg, multi, g, pl.grid, s, h->reg_staging);
             else
-                launch_gemm<EPI_GELU_SCALE_ROWMAX>(pl.cfg, g, tiles, 1, s, h->reg_staging);
+                launch_gemm<EPI_GELU_SCALE_ROWMAX>(pl.cfg, multi, g, pl.grid, s, h->reg_staging);
         });
         if (rc != LIN_EPI_OK) return rc;
-        const float *part = static_cast<const float *>(h->ws);
-        const int32_t Mi = (int32_t)M;
+        const float *part = g.out;
+        const int32_t Mi = (int32_t)M, tn = (int32_t)pl.tiles_n;
         rc = timed_launch(h, 1, [&] {
-            hipLaunchKernelGGL(rowmax_finalize_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, part, Y, Mi,
-                               (int32_t)tiles_n);
-        });
-        if (rc != LIN_EPI_OK) return rc;
-    } else if (!unfused && split > 1) {
-        const size_t bytes = (size_t)split * MN * sizeof(float);
-        rc = ensure_workspace(h, bytes);
-        if (rc != LIN_EPI_OK) return rc;
-        g.out = static_cast<float *>(h->ws);
-        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s, h->reg_staging); });
-        if (rc != LIN_EPI_OK) return rc;
-        const float *P = static_cast<const float *>(h->ws);
-        rc = timed_launch(h, 1, [&] {
-            switch (kind) {
-                case LIN_EPI_NONE: launch_reduce<EPI_NONE>(P, b, Y, MN, (int)N, split, g.tail, s); break;
-                case LIN_EPI_SCALE_HARDTANH_GELU:
-                    launch_reduce<EPI_SCALE_HARDTANH_GELU>(P, b, Y, MN, (int)N, split, g.tail, s);
-                    break;
-                default: launch_reduce<EPI_SWISH_SCALE>(P, b, Y, MN, (int)N, split, g.tail, s); break;
-            }
+            hipLaunchKernelGGL(rowmax_finalize_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, part, Y, Mi, tn);
         });
         if (rc != LIN_EPI_OK) return rc;
     } else if (!unfused) {
         g.out = Y;
         rc = timed_launch(h, 0, [&] {
             switch (kind) {
-                case LIN_EPI_NONE: launch_gemm<EPI_NONE>(pl.cfg, g, tiles, 1, s, h->reg_staging); break;
-                case LIN_EPI_SCALE_HARDTANH_GELU: launch_gemm<EPI_SCALE_HARDTANH_GELU>(pl.cfg, g, tiles, 1, s, h->reg_staging); break;
-                default: launch_gemm<EPI_SWISH_SCALE>(pl.cfg, g, tiles, 1, s, h->reg_staging); break;
+                case LIN_EPI_NONE: launch_gemm<EPI_NONE>(pl.cfg, multi, g, pl.grid, s, h->reg_staging); break;
+                case LIN_EPI_SCALE_HARDTANH_GELU:
+                    launch_gemm<EPI_SCALE_HARDTANH_GELU>(pl.cfg, multi, g, pl.grid, s, h->reg_staging);
+                    break;
+                default: launch_gemm<EPI_SWISH_SCALE>(pl.cfg, multi, g, pl.grid, s, h->reg_staging); break;
             }
         });
         if (rc != LIN_EPI_OK) return rc;
     } else {
         // Unfused ablation: raw y = XW^T + b to memory (Y itself for the
         // elementwise kinds, the workspace for the row-max kinds), then the
-        // tail as a separate pass.  Workspace: [split partials][raw y].
-        const size_t part_floats = split > 1 ? (size_t)split * MN : 0;
-        const size_t raw_floats = rowmax ? (size_t)MN : 0;
-        const size_t bytes = (part_floats + raw_floats) * sizeof(float);
-        if (bytes) {
-            rc = ensure_workspace(h, bytes);
-            if (rc != LIN_EPI_OK) return rc;
-        }
-        float *ws = static_cast<float *>(h->ws);
-        float *Yraw = rowmax ? ws + part_floats : Y;
-        if (split > 1) {
-            g.out = ws;
-            rc = timed_launch(h, 0, [&] { launch_gemm<EPI_SPLITK_PARTIAL>(pl.cfg, g, tiles, split, s, h->reg_staging); });
-            if (rc != LIN_EPI_OK) return rc;
-            rc = timed_launch(h, 1, [&] { launch_reduce<EPI_NONE>(ws, b, Yraw, MN, (int)N, split, g.tail, s); });
-            if (rc != LIN_EPI_OK) return rc;
-        } else {
-            g.out = Yraw;
-            rc = timed_launch(h, 0, [&] { launch_gemm<EPI_NONE>(pl.cfg, g, tiles, 1, s, h->reg_staging); });
-            if (rc != LIN_EPI_OK) return rc;
-        }
+        // tail as a separate pass.
+        float *Yraw = rowmax ? reinterpret_cast<float *>(ws + wl.raw) : Y;
+        g.out = Yraw;
+        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_NONE>(pl.cfg, multi, g, pl.grid, s, h->reg_staging); });
+        if (rc != LIN_EPI_OK) return rc;
         if (rowmax) {
             const int32_t pool = kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1;
             const float scale = desc->scale;
             const int32_t Ni = (int32_t)N;
             rc = timed_launch(h, 2, [&] {
-                hipLaunchKernelGGL(rowmax_pass_kernel, dim3((unsigned)M), dim3(256), 0, s, Yraw, (const float *)nullptr,
-                                   Y, MN, Ni, 1, pool, scale,
-                                   (int32_t)(N % 4 == 0 && ((uintptr_t)Yraw & 15u) == 0));
+                hipLaunchKernelGGL(rowmax_pass_kernel, dim3((unsigned)M), dim3(256), 0, s, (const float *)Yraw, Y, Ni,
+                                   pool, scale, (int32_t)(N % 4 == 0));
             });
         } else if (kind != LIN_EPI_NONE) {
+            const int64_t MN = M * N;
             const int vec4 = (MN % 4 == 0) && (((uintptr_t)Y & 15u) == 0);
             int64_t blocks = ((vec4 ? MN / 4 : MN) + 255) / 256;
             if (blocks > 65536) blocks = 65536;
@@ -602,6 +629,9 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
         }
         if (rc != LIN_EPI_OK) return rc;
     }
+    // A split run leaves its counters at zero; any run that used the
+    // workspace may have written everything past them.
+    if (split || rowmax) h->ws_clean = std::min(h->ws_clean, wl.partials);
     h->plan = plan;
     h->has_plan = true;
     return LIN_EPI_OK;

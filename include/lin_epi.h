@@ -37,9 +37,10 @@
  * Threading and streams: a handle is bound to one HIP stream at creation and
  * is not thread-safe.  lin_epi_run only enqueues work on that stream and
  * returns; the caller synchronises.  The handle owns a device workspace
- * (split-K partial sums, per-tile row maxima) that grows on demand; two runs
- * in flight on the same handle share it, which is safe because they are
- * ordered on the handle's stream.
+ * (partial sums of output tiles split over workgroups, their arrival
+ * counters, per-tile row maxima) that grows on demand; two runs in flight
+ * on the same handle share it, which is safe because they are ordered on the
+ * handle's stream.
  *
  * Errors: every call returns a status code (LIN_EPI_OK = 0 or a negative
  * LIN_EPI_E* value).  Arguments are validated on the host before any HIP
@@ -88,10 +89,23 @@ enum {
  * stream).  Makes no device allocation.  *out is set to NULL on failure. */
 int lin_epi_create(lin_epi_handle *out, void *hip_stream);
 
-/* Enqueue Y = tail(X W^T + b) on the handle's stream.
+/* Enqueue Y = tail(X W^T + b) on the handle's stream: the forward pass of
+ * the pages' model (page "Kimi-K2.6 l2_p53", its ModelNew.forward: the
+ * linear layer with weight [out, in] and bias, then the tail), with the tail
+ * chosen by desc->kind and the layer's parameters passed per call.
+ *   X  [M, K] device, read only       W [N, K] device, read only
+ *   b  [N]    device, read only       Y [M, N] (kinds 0, 1, 3) or [M]
+ *                                       (kinds 2, 4) device, written
+ * The caller owns every buffer and keeps it alive until the stream reaches
+ * the end of the call; the handle's workspace holds any intermediate
+ * (K-slice partial sums, per-tile row maxima).
  * M == 0 or N == 0 is a successful no-op.  K == 0 is allowed and gives
  * Y = tail(b) broadcast over the rows (the empty sum is 0); X and W may then
- * be NULL.  b must not be NULL (every layer on the pages has a bias). */
+ * be NULL.  b must not be NULL (every layer on the pages has a bias).
+ * Errors: EINVAL (null handle, desc, b or Y, or X/W with K > 0; negative or
+ * > INT32_MAX sizes; unknown kind; ht_min > ht_max), EALIGN, ENOTSUP (kind 2
+ * with another window or N < 16), ENOMEM (workspace), EHIP (launch); on an
+ * error nothing is enqueued. */
 int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K,
                 const float *X, const float *W, const float *b,
                 const lin_epi_desc *desc, float *Y);
@@ -135,10 +149,11 @@ int lin_epi_scale_weights(lin_epi_handle h, int64_t N, int64_t K, const float *W
 /* ---- tuning and introspection (not needed for ordinary use) ------------- */
 
 enum {
-    /* Split-K control: 0 = automatic (default), 1 = never split, S >= 2 =
-     * split K into S slices whose partial sums are added in slice order by
-     * a second pass (deterministic) that also applies the tail (for the
-     * row-max kinds: bias, pooling, GELU, scale and the max). */
+    /* Split-K control: 0 = automatic (default), 1 = never split (one
+     * output tile per workgroup), S >= 2 = every output tile computed in S
+     * K segments by S workgroups (clamped to the K steps available).  The
+     * last of a tile's workgroups to finish adds the segments' partial sums
+     * in K order, so results are the same on every run. */
     LIN_EPI_OPT_SPLIT_K = 1,
     /* 1 = time every kernel this handle launches with HIP events on its
      * stream (read with lin_epi_profile_read); 0 = off (default). */
@@ -159,7 +174,13 @@ enum {
      * 0 = automatic (default).  Both stagings feed the same MFMA sequence,
      * so results are bit-identical; exists to test and measure the
      * direct-to-LDS path against the other one. */
-    LIN_EPI_OPT_REG_STAGING = 5
+    LIN_EPI_OPT_REG_STAGING = 5,
+    /* Stream-K grid: 0 = automatic (default), G >= 1 = run the GEMM with G
+     * workgroups that divide the (tile, K step) work into G contiguous
+     * ranges, balanced to within one K step (clamped to the work available);
+     * tiles a range boundary cuts are finished as with LIN_EPI_OPT_SPLIT_K.
+     * Overrides LIN_EPI_OPT_SPLIT_K. */
+    LIN_EPI_OPT_GRID = 6
 };
 
 int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value);
@@ -167,10 +188,13 @@ int lin_epi_set_option(lin_epi_handle h, int32_t option, int64_t value);
 /* What the last successful lin_epi_run launched. */
 typedef struct {
     int32_t tile_m, tile_n, tile_k; /* workgroup output tile and K step */
-    int32_t split_k;                /* K slices (1 = no split) */
+    int32_t split_k;                /* most K segments any output tile is cut into (1 = none) */
     int64_t grid_main;              /* workgroups of the GEMM kernel */
-    int32_t kernels;                /* kernels launched (GEMM + reduce/finalize/tail) */
+    int32_t kernels;                /* kernels launched (GEMM + row-max finalize or unfused tail) */
     int64_t workspace_bytes;        /* workspace the run used */
+    int32_t schedule;               /* 0: one output tile per workgroup; 1: split-K, grid = tiles *
+                                       split_k, equal K segments; 2: stream-K, workgroup ranges
+                                       cross tile boundaries */
 } lin_epi_plan;
 
 int lin_epi_last_plan(lin_epi_handle h, lin_epi_plan *out);
@@ -185,8 +209,8 @@ int lin_epi_query_plan(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const 
 
 /* Accumulated kernel timings since the last read (profiling on).  Waits for
  * the handle's stream.  Role 0 is the GEMM kernel, role 1 the second pass
- * (split-K reduce or row-max finalize), role 2 the separate tail kernel of
- * the unfused ablation and lin_epi_pool_weights. */
+ * (row-max finalize), role 2 the separate tail kernel of the unfused
+ * ablation, lin_epi_pool_weights and lin_epi_scale_weights. */
 typedef struct {
     int64_t launches[3];
     double total_ms[3];

@@ -60,7 +60,15 @@ int main(void)
     CHECK(p.tile_m == 256 && p.tile_n == 256 && p.split_k == 1 && p.grid_main == 256 && p.kernels == 1);
     CHECK(lin_epi_set_option(h, LIN_EPI_OPT_TILE, 0) == LIN_EPI_OK);
     CHECK(lin_epi_query_plan(h, 128, 32768, 32768, &d, 256, &p) == LIN_EPI_OK);
-    CHECK(p.tile_m == 128 && p.split_k >= 2 && p.workspace_bytes == (int64_t)p.split_k * 128 * 32768 * 4);
+    /* 128 tiles of 128x256 split over 256 workgroups: one partial-sum slot
+     * of 128x256 floats per workgroup after the per-tile counters */
+    CHECK(p.tile_m == 128 && p.split_k >= 2 && p.schedule == 1 && p.kernels == 1);
+    CHECK(p.workspace_bytes >= p.grid_main * 128 * 256 * 4);
+    CHECK(lin_epi_set_option(h, LIN_EPI_OPT_GRID, 300) == LIN_EPI_OK);
+    CHECK(lin_epi_query_plan(h, 128, 32768, 32768, &d, 256, &p) == LIN_EPI_OK);
+    CHECK(p.grid_main == 300 && p.schedule == 2);
+    CHECK(lin_epi_set_option(h, LIN_EPI_OPT_GRID, -1) == LIN_EPI_EINVAL);
+    CHECK(lin_epi_set_option(h, LIN_EPI_OPT_GRID, 0) == LIN_EPI_OK);
     CHECK(lin_epi_last_plan(h, &p) == LIN_EPI_EINVAL); /* nothing has run */
     CHECK(lin_epi_profile_read(h, &prof) == LIN_EPI_OK && prof.launches[0] == 0);
 

@@ -147,7 +147,8 @@ int main(void)
         CHECK(lin_epi_set_option(hs, LIN_EPI_OPT_SPLIT_K, 3) == LIN_EPI_OK);
         CHECK(lin_epi_run(hs, M, N, K, in.dX, in.dW, in.db, &d, dY) == LIN_EPI_OK);
         HIP_OK(hipStreamSynchronize(stream));
-        CHECK(lin_epi_last_plan(hs, &plan) == LIN_EPI_OK && plan.split_k == 3 && plan.kernels == 2);
+        CHECK(lin_epi_last_plan(hs, &plan) == LIN_EPI_OK && plan.split_k == 3 && plan.kernels == 1 &&
+              plan.schedule == 1);
         HIP_OK(hipMemcpy(Y, dY, sizeof(float) * (size_t)(M * N), hipMemcpyDeviceToHost));
         oracle_tail_scale_hardtanh_gelu(y, M * N, 0.5, -2.0, 2.0, ref);
         for (i = 0; i < M * N; ++i) bad += !close_enough(Y[i], ref[i]);

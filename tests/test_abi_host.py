@@ -105,6 +105,10 @@ def test_options_and_introspection_validation(handle):
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_REG_STAGING, 2) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_REG_STAGING, 1) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_REG_STAGING, 0) == lib.LIN_EPI_OK
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, -1) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 2**31) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 300) == lib.LIN_EPI_OK
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 0) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 6) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, -1) == lib.LIN_EPI_EINVAL
     for t in range(6):
@@ -169,7 +173,7 @@ def test_destroy_null_is_noop():
 
 def test_desc_layout_matches_header():
     assert ctypes.sizeof(lib.lin_epi_desc) == 24
-    assert ctypes.sizeof(lib.lin_epi_plan) == 40
+    assert ctypes.sizeof(lib.lin_epi_plan) == 48
     assert ctypes.sizeof(lib.lin_epi_profile) == 48
 
 
@@ -178,31 +182,64 @@ def test_desc_layout_matches_header():
 def _plan(handle, M, N, K, kind, cus=256):
     rc, p = lib.lin_epi_query_plan(handle, M, N, K, lib.make_desc(kind, 1.0), cus)
     assert rc == lib.LIN_EPI_OK, lib.lin_epi_status_string(rc)
-    return (p.tile_m, p.tile_n, p.split_k, p.kernels, p.grid_main, p.workspace_bytes)
+    return (p.tile_m, p.tile_n, p.split_k, p.kernels, p.grid_main, p.workspace_bytes, p.schedule)
 
 
 def test_planner_choices_for_the_workloads(handle):
     A, B, C, F = (lib.LIN_EPI_SCALE_HARDTANH_GELU, lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX, lib.LIN_EPI_SWISH_SCALE,
                   lib.LIN_EPI_GELU_SCALE_ROWMAX)
-    # 2048x8192x8192: 256x256 tiles, one per compute unit, no split
-    assert _plan(handle, 2048, 8192, 8192, A) == (256, 256, 1, 1, 256, 0)
-    # 128x32768x32768: 128x256 tiles (128 of them) split in two
-    assert _plan(handle, 128, 32768, 32768, C)[:4] == (128, 256, 2, 2)
-    # ragged: 8x47 tiles of 128x128 (two per compute unit), two K slices -> 752 workgroups
-    assert _plan(handle, 1000, 6000, 4100, A)[:5] == (128, 128, 2, 2, 752)
-    # pooled-weight tail (b): a 1024x512x8192 GEMM is split into 8 K slices to fill the device
-    assert _plan(handle, 1024, 512, 8192, F)[:4] == (128, 128, 8, 2)
-    # few rows against a long weight stream: 32x128 tiles, split so that two
-    # workgroups per compute unit stream W (512 workgroups)
-    assert _plan(handle, 16, 32768, 32768, C)[:5] == (32, 128, 2, 2, 512)
-    assert _plan(handle, 1, 32768, 32768, C)[:5] == (32, 128, 2, 2, 512)
-    assert _plan(handle, 16, 8192, 8192, C)[:5] == (32, 128, 8, 2, 512)
-    # tail (b) unsplit keeps per-tile row maxima: M * tiles_n floats
+    # 2048x8192x8192: 256x256 tiles, one per compute unit, no split, no workspace
+    assert _plan(handle, 2048, 8192, 8192, A) == (256, 256, 1, 1, 256, 0, 0)
+    # 128x32768x32768: 128x256 tiles (128 of them) split in two, finished in
+    # the GEMM kernel itself (one kernel)
+    assert _plan(handle, 128, 32768, 32768, C)[:5] == (128, 256, 2, 1, 256)
+    # tail (b) at 1024x8192x8192: whatever the split, the partial sums that
+    # reach memory are pooled windows (16x smaller than the raw [M, N] slices,
+    # 64 MiB at two slices) plus the per-tile row maxima
     t = _plan(handle, 1024, 8192, 8192, B)
-    if t[2] == 1:
-        assert t[5] == 1024 * (8192 // t[1]) * 4
-    else:
-        assert t[5] == t[2] * 1024 * 8192 * 4
+    assert t[3] == 2 and t[5] < 16 * 2**20, t
+    # every elementwise plan is one kernel; the ragged shape uses a split grid
+    t = _plan(handle, 1000, 6000, 4100, A)
+    assert t[3] == 1 and t[6] >= 1, t
+    # few rows against a long weight stream: 32x128 tiles, at least two
+    # workgroups per compute unit stream W
+    for M in (1, 8, 16):
+        t = _plan(handle, M, 32768, 32768, C)
+        assert t[:2] == (32, 128) and t[4] >= 512, t
+
+
+def test_planner_page2_never_writes_raw_partials(handle):
+    """Tail (b) splits only with pooled partial sums: the workspace holds
+    per-tile counters, two slots of (tile / 16) floats per workgroup and the
+    per-tile row maxima, never the [M, N] linear output."""
+    B = lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX
+    for S in (0, 2, 3, 5):
+        assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, S) == 0
+        tm, tn, s, k, grid, ws, sched = _plan(handle, 1024, 8192, 8192, B)
+        tiles = -(-1024 // tm) * -(-8192 // tn)
+        slots = grid * (2 if sched == 2 else 1)
+        bound = tiles * 4 + 256 + slots * tm * tn // 16 * 4 + 256 + 1024 * (8192 // tn) * 4 + 256
+        assert ws <= bound, (S, ws, bound)
+        # raw [M, N] slices would take s * 32 MiB; pooled ones a sixteenth
+        assert ws < s * 1024 * 8192 * 4 // 8, (S, ws)
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 0) == 0
+
+
+def test_planner_grid_option(handle):
+    """LIN_EPI_OPT_GRID forces a stream-K grid (clamped to the work), and
+    overrides the split option."""
+    A = lib.LIN_EPI_SCALE_HARDTANH_GELU
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 3) == 0
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 300) == 0
+    t = _plan(handle, 1000, 6000, 4100, A)
+    assert t[4] == 300 and t[6] == 2
+    # a grid larger than the (tile, K step) work is clamped to it
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 4) == 0
+    t = _plan(handle, 64, 64, 64, A)
+    assert t[4] == 2
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 0) == 0
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 0) == 0
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 0) == 0
 
 
 def test_planner_respects_options(handle):
@@ -230,8 +267,8 @@ def test_planner_tile_override(handle):
 def test_planner_small_problems_spread_out(handle):
     # 64x256x256 would be one 128x256 workgroup; the planner spreads it over
     # 64x64 tiles and K slices instead
-    tm, tn, s, k, grid, _ = _plan(handle, 64, 256, 256, lib.LIN_EPI_SCALE_HARDTANH_GELU)
-    assert (tm, tn) == (64, 64) and grid >= 16
+    tm, tn, s, k, grid, _, _ = _plan(handle, 64, 256, 256, lib.LIN_EPI_SCALE_HARDTANH_GELU)
+    assert (tm, tn) == (64, 64) and grid >= 4
 
 
 def test_planner_every_slice_gets_k(handle):
@@ -240,7 +277,7 @@ def test_planner_every_slice_gets_k(handle):
     for K in (4, 32, 36, 100, 1000, 4100):
         for S in (2, 3, 5, 16):
             assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, S) == 0
-            tm, tn, s, _, grid, _ = _plan(handle, 300, 300, K, lib.LIN_EPI_NONE)
+            tm, tn, s, _, grid, _, _ = _plan(handle, 300, 300, K, lib.LIN_EPI_NONE)
             assert 1 <= s <= max(1, -(-K // 32))
             assert grid == -(-300 // tm) * -(-300 // tn) * s
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 0) == 0

@@ -21,8 +21,8 @@ def test_c_program_runs_the_hot_path_on_the_gpu():
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    if not os.path.exists(BIN):
-        pytest.skip("tests/c_abi_gpu.bin is not built (python -c 'import __graft_entry__ as g; g.build()')")
+    # build() always produces the binary, so its absence is a failure, not a skip
+    assert os.path.exists(BIN), "tests/c_abi_gpu.bin is not built (python -c 'import __graft_entry__ as g; g.build()')"
     log("== running %s" % BIN)
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
     out = r.stdout + r.stderr
