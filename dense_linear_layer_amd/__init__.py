@@ -29,6 +29,7 @@ LIN_EPI_EALIGN = -2
 LIN_EPI_ENOTSUP = -3
 LIN_EPI_ENOMEM = -4
 LIN_EPI_EHIP = -5
+LIN_EPI_ETOOBIG = -6
 
 # options
 LIN_EPI_OPT_SPLIT_K = 1
@@ -43,6 +44,8 @@ TILE_CONFIGS = {1: (256, 256), 2: (128, 256), 3: (128, 128), 4: (64, 64), 5: (32
 EXPORTS = (
     "lin_epi_create",
     "lin_epi_run",
+    "lin_epi_run_noalloc",
+    "lin_epi_noalloc_scratch_bytes",
     "lin_epi_destroy",
     "lin_epi_status_string",
     "lin_epi_pool_weights",
@@ -107,6 +110,10 @@ def load_library():
     lib.lin_epi_create.restype = ctypes.c_int
     lib.lin_epi_run.argtypes = [p, i64, i64, i64, p, p, p, ctypes.POINTER(lin_epi_desc), p]
     lib.lin_epi_run.restype = ctypes.c_int
+    lib.lin_epi_run_noalloc.argtypes = [p, i64, i64, i64, p, p, p, ctypes.POINTER(lin_epi_desc), p]
+    lib.lin_epi_run_noalloc.restype = ctypes.c_int
+    lib.lin_epi_noalloc_scratch_bytes.argtypes = []
+    lib.lin_epi_noalloc_scratch_bytes.restype = i64
     lib.lin_epi_destroy.argtypes = [p]
     lib.lin_epi_destroy.restype = ctypes.c_int
     lib.lin_epi_status_string.argtypes = [ctypes.c_int]
@@ -147,6 +154,18 @@ def lin_epi_run(handle: int, M: int, N: int, K: int, X: int, W: int, b: int, des
     return load_library().lin_epi_run(ctypes.c_void_p(handle or None), M, N, K, ctypes.c_void_p(X or None),
                                       ctypes.c_void_p(W or None), ctypes.c_void_p(b or None), d,
                                       ctypes.c_void_p(Y or None))
+
+
+def lin_epi_run_noalloc(handle: int, M: int, N: int, K: int, X: int, W: int, b: int, desc: lin_epi_desc | None,
+                        Y: int) -> int:
+    d = ctypes.byref(desc) if desc is not None else None
+    return load_library().lin_epi_run_noalloc(ctypes.c_void_p(handle or None), M, N, K, ctypes.c_void_p(X or None),
+                                              ctypes.c_void_p(W or None), ctypes.c_void_p(b or None), d,
+                                              ctypes.c_void_p(Y or None))
+
+
+def lin_epi_noalloc_scratch_bytes() -> int:
+    return int(load_library().lin_epi_noalloc_scratch_bytes())
 
 
 def lin_epi_destroy(handle: int) -> int:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -254,6 +255,32 @@ struct Plan {
     int steps;
 };
 
+// Workspace layout of one run: [arrival counters, one int per tile, rounded
+// up to 256 bytes][partial-sum slots when tiles are split: one per
+// workgroup for split-K, two for stream-K][row-max partials M * tiles_n]
+// [raw linear output M * N: unfused row-max tails only].
+struct WsLayout {
+    size_t counters, partials, rowmax, raw, total;  // byte offsets and size
+};
+
+WsLayout ws_layout(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, int kind)
+{
+    WsLayout w{};
+    const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
+    const bool split = pl.segments > tiles;
+    const int64_t slot = (int64_t)kCfgs[pl.cfg].bm * kCfgs[pl.cfg].bn /
+                         (!h->unfused && kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    w.counters = 0;
+    w.partials = up((size_t)tiles * sizeof(int32_t));
+    const int64_t nslots = pl.schedule == 2 ? 2 * pl.grid : pl.grid;  // split-K never crosses a tile
+    w.rowmax = w.partials + (split ? up((size_t)(nslots * slot) * sizeof(float)) : 0);
+    const bool rm = is_rowmax(kind);
+    w.raw = w.rowmax + (rm && !h->unfused ? up((size_t)(M * pl.tiles_n) * sizeof(float)) : 0);
+    w.total = w.raw + (rm && h->unfused ? up((size_t)(M * N) * sizeof(float)) : 0);
+    return w;
+}
+
 // Pick the tile configuration and the grid by estimated time.  For each
 // configuration the candidate grids are one tile per workgroup, split-K
 // with S = 2..16 equal K segments per tile (at most one per K step), and
@@ -270,10 +297,15 @@ struct Plan {
 // estimate wins.  LIN_EPI_OPT_SPLIT_K = 1 forbids splitting, S >= 2 forces
 // S segments per tile (clamped to the K steps available);
 // LIN_EPI_OPT_GRID = G forces a grid of G workgroups (clamped to T).
-Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind, int num_cus)
+// Plans whose workspace exceeds max_ws are skipped; *fits reports whether
+// any plan was left (with a fixed workspace a large row-max problem may
+// have none).
+Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind, int num_cus,
+                 size_t max_ws = SIZE_MAX, bool *fits = nullptr)
 {
     Plan best{CFG_SMALL, 1, 0, 1, 1, 1, 1, 1};
     double best_t = 1e300;
+    bool any = false;
     const bool rowmax = is_rowmax(kind);
     const int steps = k_steps((int)K);
     for (int c = 0; c < CFG_COUNT; ++c) {
@@ -318,40 +350,19 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
                 t += kFixupFixedS + 2.0 * (double)(st.segments - tiles) * slot_bytes / kPassBytesPerS +
                      (st.max_per_tile - 1) * slot_bytes / kCuBytesPerS;
             if (rowmax) t += kPassFixedS;
+            const Plan cand{c, G, G == tiles ? 0 : G % tiles == 0 ? 1 : 2, st.max_per_tile, st.segments,
+                            (int)tm, (int)tn, steps};
+            if (max_ws != SIZE_MAX && (st.segments > tiles || rowmax) && ws_layout(h, cand, M, N, kind).total > max_ws)
+                continue;
             if (t < best_t) {
                 best_t = t;
-                best = Plan{c, G, G == tiles ? 0 : G % tiles == 0 ? 1 : 2, st.max_per_tile, st.segments,
-                            (int)tm, (int)tn, steps};
+                best = cand;
+                any = true;
             }
         }
     }
+    if (fits) *fits = any;
     return best;
-}
-
-// Workspace layout of one run: [arrival counters, one int per tile, rounded
-// up to 256 bytes][partial-sum slots when tiles are split: one per
-// workgroup for split-K, two for stream-K][row-max partials M * tiles_n]
-// [raw linear output M * N: unfused row-max tails only].
-struct WsLayout {
-    size_t counters, partials, rowmax, raw, total;  // byte offsets and size
-};
-
-WsLayout ws_layout(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, int kind)
-{
-    WsLayout w{};
-    const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
-    const bool split = pl.segments > tiles;
-    const int64_t slot = (int64_t)kCfgs[pl.cfg].bm * kCfgs[pl.cfg].bn /
-                         (!h->unfused && kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);
-    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    w.counters = 0;
-    w.partials = up((size_t)tiles * sizeof(int32_t));
-    const int64_t nslots = pl.schedule == 2 ? 2 * pl.grid : pl.grid;  // split-K never crosses a tile
-    w.rowmax = w.partials + (split ? up((size_t)(nslots * slot) * sizeof(float)) : 0);
-    const bool rm = is_rowmax(kind);
-    w.raw = w.rowmax + (rm && !h->unfused ? up((size_t)(M * pl.tiles_n) * sizeof(float)) : 0);
-    w.total = w.raw + (rm && h->unfused ? up((size_t)(M * N) * sizeof(float)) : 0);
-    return w;
 }
 
 // The launch plan of one lin_epi_run call as the C interface reports it.
@@ -409,6 +420,7 @@ const char *lin_epi_status_string(int status)
         case LIN_EPI_ENOTSUP: return "unsupported tail parameters";
         case LIN_EPI_ENOMEM: return "device workspace allocation failed";
         case LIN_EPI_EHIP: return "HIP call or kernel launch failed";
+        case LIN_EPI_ETOOBIG: return "problem needs more workspace than the fixed no-alloc scratch array holds";
         default: return "unknown status";
     }
 }
@@ -505,8 +517,24 @@ int lin_epi_profile_read(lin_epi_handle h, lin_epi_profile *out)
     return rc;
 }
 
-int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, const float *W, const float *b,
-                const lin_epi_desc *desc, float *Y)
+}  // extern "C"
+
+namespace {
+
+// A workspace in place of the handle's own: fixed size, never (re)allocated;
+// its arrival counters are cleared on every call that splits tiles.
+struct FixedWs {
+    char *base;
+    size_t bytes;
+};
+
+int scratch_address(int dev, char **out);
+extern const size_t kScratchBytesHost;
+
+// lin_epi_run (noalloc = false) and lin_epi_run_noalloc (true): the same
+// validation, plan and kernels; only where intermediates live differs.
+int run_impl(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, const float *W, const float *b,
+             const lin_epi_desc *desc, float *Y, bool noalloc)
 {
     // ---- validation: host only, before any HIP call
     if (!h) return LIN_EPI_EINVAL;
@@ -522,10 +550,20 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
 
     rc = ensure_device(h);
     if (rc != LIN_EPI_OK) return rc;
+    FixedWs fixed_ws{nullptr, 0};
+    const FixedWs *fixed = nullptr;
+    if (noalloc) {
+        rc = scratch_address(h->device, &fixed_ws.base);
+        if (rc != LIN_EPI_OK) return rc;
+        fixed_ws.bytes = kScratchBytesHost;
+        fixed = &fixed_ws;
+    }
 
     const bool rowmax = is_rowmax(kind);
     const bool unfused = h->unfused;
-    const Plan pl = choose_plan(h, M, N, K, kind, h->num_cus);
+    bool fits = true;
+    const Plan pl = choose_plan(h, M, N, K, kind, h->num_cus, fixed ? fixed->bytes : SIZE_MAX, &fits);
+    if (!fits) return LIN_EPI_ETOOBIG;
     const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
     const lin_epi_plan plan = describe(h, pl, M, N, kind);
     const WsLayout wl = ws_layout(h, pl, M, N, kind);
@@ -550,7 +588,19 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
     g.tail = TailParams{desc->scale, desc->ht_min, desc->ht_max};
 
     char *ws = nullptr;
-    if (split || rowmax) {
+    if ((split || rowmax) && fixed) {
+        ws = fixed->base;
+        if (split) {
+            // the fixed array keeps whatever the last call left: clear the
+            // arrival counters (a fill kernel, not a memset)
+            const int64_t n = (int64_t)(wl.partials / sizeof(int32_t));
+            const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
+            hipLaunchKernelGGL(zero_counters_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<int32_t *>(ws), n);
+            if (hipGetLastError() != hipSuccess) return LIN_EPI_EHIP;
+        }
+        g.counters = reinterpret_cast<int32_t *>(ws + wl.counters);
+        g.partials = reinterpret_cast<float *>(ws + wl.partials);
+    } else if (split || rowmax) {
         rc = ensure_workspace(h, wl.total);
         if (rc != LIN_EPI_OK) return rc;
         ws = static_cast<char *>(h->ws);
@@ -631,10 +681,69 @@ int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *
     }
     // A split run leaves its counters at zero; any run that used the
     // workspace may have written everything past them.
-    if (split || rowmax) h->ws_clean = std::min(h->ws_clean, wl.partials);
+    if (!fixed && (split || rowmax)) h->ws_clean = std::min(h->ws_clean, wl.partials);
     h->plan = plan;
     h->has_plan = true;
     return LIN_EPI_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch for lin_epi_run_noalloc: every intermediate of a run
+// (arrival counters, partial sums of split tiles, per-tile row maxima) in
+// one file-scope device array instead of the handle's workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code the array's name is not a device address: its address on each device
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+const size_t kScratchBytesHost = kScratchBytes;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kMaxDevices];
+
+int scratch_address(int dev, char **out)
+{
+    if (dev < 0 || dev >= kMaxDevices) return LIN_EPI_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || cur != dev) return LIN_EPI_EINVAL;
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return LIN_EPI_EHIP;
+        }
+        g_scratch_ptr[dev] = static_cast<char *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return LIN_EPI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, const float *W, const float *b,
+                const lin_epi_desc *desc, float *Y)
+{
+    return run_impl(h, M, N, K, X, W, b, desc, Y, false);
+}
+
+int lin_epi_run_noalloc(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, const float *W,
+                        const float *b, const lin_epi_desc *desc, float *Y)
+{
+    return run_impl(h, M, N, K, X, W, b, desc, Y, true);
+}
+
+int64_t lin_epi_noalloc_scratch_bytes(void)
+{
+    return (int64_t)kScratchBytes;
 }
 
 int lin_epi_query_plan(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const lin_epi_desc *desc,

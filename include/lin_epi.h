@@ -82,7 +82,9 @@ enum {
     LIN_EPI_EALIGN = -2,  /* X or W not 16-byte aligned, K % 4 != 0, Y not 4-byte aligned */
     LIN_EPI_ENOTSUP = -3, /* kind 2 with pool_kernel != 16, pool_stride != pool_kernel, or N < 16 */
     LIN_EPI_ENOMEM = -4,  /* workspace allocation failed */
-    LIN_EPI_EHIP = -5     /* a HIP call or kernel launch failed */
+    LIN_EPI_EHIP = -5,    /* a HIP call or kernel launch failed */
+    LIN_EPI_ETOOBIG = -6  /* lin_epi_run_noalloc: the problem needs more workspace than the fixed
+                             scratch array holds (lin_epi_noalloc_scratch_bytes) */
 };
 
 /* Create a handle bound to `hip_stream` (a hipStream_t; NULL = the default
@@ -109,6 +111,26 @@ int lin_epi_create(lin_epi_handle *out, void *hip_stream);
 int lin_epi_run(lin_epi_handle h, int64_t M, int64_t N, int64_t K,
                 const float *X, const float *W, const float *b,
                 const lin_epi_desc *desc, float *Y);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments, errors and kernels as lin_epi_run, with every
+ * intermediate (arrival counters of split tiles, their partial sums, per-tile
+ * row maxima) in a fixed device array of lin_epi_noalloc_scratch_bytes()
+ * bytes (64 MiB) that the library holds on each GPU it runs on until the
+ * process ends, instead of the handle's workspace.  Makes no allocation of
+ * any kind: the plan is chosen among those whose intermediates fit, and a
+ * problem with none (a row-max tail with very many rows) returns
+ * LIN_EPI_ETOOBIG before anything is enqueued.  The handle's device must be
+ * the current device.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other handles, other threads) race
+ * and give wrong results; calls ordered on one stream are safe. */
+int lin_epi_run_noalloc(lin_epi_handle h, int64_t M, int64_t N, int64_t K,
+                        const float *X, const float *W, const float *b,
+                        const lin_epi_desc *desc, float *Y);
+
+/* Size in bytes of the fixed scratch array lin_epi_run_noalloc uses. */
+int64_t lin_epi_noalloc_scratch_bytes(void);
 
 /* Release the handle and its workspace (waits for the handle's stream
  * first).  NULL is a no-op. */

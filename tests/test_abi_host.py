@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert lib.lin_epi_status_string(0) == "ok"
-    for code in (-1, -2, -3, -4, -5):
+    for code in (-1, -2, -3, -4, -5, -6):
         assert lib.lin_epi_status_string(code) not in ("ok", "unknown status")
     assert lib.lin_epi_status_string(42) == "unknown status"
 
@@ -292,3 +292,28 @@ def test_query_plan_validation(handle):
     assert lib.lin_epi_query_plan(handle, 8, 8, 8, lib.make_desc(2, pool_kernel=4), 256)[0] == lib.LIN_EPI_ENOTSUP
     rc, p = lib.lin_epi_query_plan(handle, 0, 8, 8, d, 256)
     assert rc == 0 and p.grid_main == 0
+
+
+# ---- the allocation-free entry point: host-side behaviour ------------------
+
+def test_noalloc_scratch_size():
+    assert lib.lin_epi_noalloc_scratch_bytes() == 64 * 2**20
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(h=0), lib.LIN_EPI_EINVAL),
+    (dict(desc=None), lib.LIN_EPI_EINVAL),
+    (dict(M=-1), lib.LIN_EPI_EINVAL),
+    (dict(K=6), lib.LIN_EPI_EALIGN),
+    (dict(M=0), lib.LIN_EPI_OK),
+    (dict(N=0), lib.LIN_EPI_OK),
+    (dict(b=0), lib.LIN_EPI_EINVAL),
+    (dict(desc=lib.make_desc(2, pool_kernel=8)), lib.LIN_EPI_ENOTSUP),
+])
+def test_noalloc_validation_before_any_hip_call(handle, args, expect):
+    """lin_epi_run_noalloc validates exactly as lin_epi_run does, on the host,
+    before touching the device (this container has no GPU)."""
+    a = dict(h=handle, M=8, N=32, K=16, X=A16, W=A16, b=A16, desc=DESC_A, Y=A16)
+    a.update(args)
+    rc = lib.lin_epi_run_noalloc(a["h"], a["M"], a["N"], a["K"], a["X"], a["W"], a["b"], a["desc"], a["Y"])
+    assert rc == expect, lib.lin_epi_status_string(rc)

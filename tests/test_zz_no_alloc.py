@@ -1,0 +1,135 @@
+"""The allocation-free entry point lin_epi_run_noalloc, called through the C
+ABI, against lin_epi_run on the same inputs: the same kernels with every
+intermediate in the library's fixed device scratch array instead of the
+handle's workspace.  Where both pick the same plan the outputs must be
+bitwise equal; otherwise (the fixed array rules out plans whose
+intermediates do not fit) within 1e-3 * (1 + |ref|) of lin_epi_run and of
+the oracle.  Calls follow each other on one stream, the later ones smaller,
+so leftovers of an earlier call in the shared array (arrival counters,
+partial sums) would show."""
+
+import numpy as np
+import pytest
+
+import dense_linear_layer_amd as lib
+import oracle
+import workloads
+from parity_util import compare, desc_for, log, oracle_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    log("== %s" % request.node.nodeid)
+
+
+def _noalloc(h, Xd, Wd, bd, tail, Y):
+    M, K = Xd.shape
+    N = Wd.shape[0]
+    rc = lib.lin_epi_run_noalloc(h.handle, M, N, K, Xd.data_ptr(), Wd.data_ptr(), bd.data_ptr(), desc_for(tail),
+                                 Y.data_ptr())
+    assert rc == lib.LIN_EPI_OK, lib.lin_epi_status_string(rc)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy(), h.plan()
+
+
+def _regular(h, Xd, Wd, bd, tail, Y):
+    h.run_into(Xd, Wd, bd, desc_for(tail), Y)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy(), h.plan()
+
+
+def _same_plan(p, q):
+    return (p.tile_m, p.tile_n, p.grid_main, p.schedule) == (q.tile_m, q.tile_n, q.grid_main, q.schedule)
+
+
+# (M, N, K, tail, options): split plans of every kind, stream-K, and the
+# planner's own choices; each sequence ends with smaller problems
+SEQUENCES = {
+    "split_then_smaller": [
+        (300, 530, 1028, workloads.TAIL_A, dict(grid=301, tile=4)),
+        (64, 64, 100, workloads.TAIL_A, dict(split=3, tile=4)),
+    ],
+    "rowmax_then_smaller": [
+        (500, 3000, 520, workloads.TAIL_B, dict(split=3)),
+        (40, 400, 36, workloads.TAIL_B, dict(split=2, tile=3)),
+    ],
+    "folded_then_elementwise": [
+        (257, 512, 2052, workloads.TAIL_B_FOLDED, dict(grid=200, tile=3)),
+        (130, 290, 100, workloads.TAIL_C, dict(split=5, tile=2)),
+        (33, 17, 4, workloads.TAIL_NONE, dict(split=1)),
+    ],
+    "planner_choice": [
+        (1000, 6000, 4100, workloads.TAIL_A, dict()),
+        (1000, 6000, 4100, workloads.TAIL_B, dict()),
+        (128, 1024, 8192, workloads.TAIL_C, dict()),
+    ],
+}
+
+
+@pytest.mark.parametrize("name", sorted(SEQUENCES))
+def test_noalloc_matches_run(name):
+    with lib.LinEpi() as h:
+        for M, N, K, tail, opt in SEQUENCES[name]:
+            X, W, b = workloads.make_inputs(M, N, K, seed=M + 3 * N + 7 * K)
+            Xd, Wd, bd = to_dev(X, W, b)
+            Y = torch.empty(lib.LinEpi.output_shape(M, N, tail.kind), dtype=torch.float32, device="cuda:0")
+            h.set_option(lib.LIN_EPI_OPT_TILE, opt.get("tile", 0))
+            h.set_option(lib.LIN_EPI_OPT_SPLIT_K, opt.get("split", 0))
+            h.set_option(lib.LIN_EPI_OPT_GRID, opt.get("grid", 0))
+            log("%dx%dx%d %s %s" % (M, N, K, tail.name, opt))
+            # twice in a row through the fixed array, then the regular path
+            got1, p1 = _noalloc(h, Xd, Wd, bd, tail, Y)
+            Y.fill_(float("nan"))
+            got2, p2 = _noalloc(h, Xd, Wd, bd, tail, Y)
+            Y.fill_(float("nan"))
+            ref_run, pr = _regular(h, Xd, Wd, bd, tail, Y)
+            log("plans: noalloc tile %dx%d grid %d schedule %d; run tile %dx%d grid %d schedule %d" % (
+                p1.tile_m, p1.tile_n, p1.grid_main, p1.schedule, pr.tile_m, pr.tile_n, pr.grid_main, pr.schedule))
+            assert p1.workspace_bytes <= lib.lin_epi_noalloc_scratch_bytes()
+            assert np.array_equal(got1, got2), "two no-alloc calls differ"
+            if _same_plan(p1, pr):
+                assert np.array_equal(got1, ref_run), "same plan, different result"
+            else:
+                compare(got1, ref_run, what="noalloc vs run %s" % tail.name)
+            compare(got1, oracle_rows(X, W, b, tail), what="noalloc vs oracle %s" % tail.name)
+
+
+def test_noalloc_integer_exact_after_larger_call():
+    """A split call that leaves its partial sums in the array, then a smaller
+    split call on integer inputs: bit-exact, so nothing of the first leaks."""
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_TILE, 3)
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, 4)
+        for M, N, K in ((700, 900, 2100), (70, 90, 260)):
+            X, W, b = workloads.integer_inputs(M, N, K, seed=M + N)
+            Xd, Wd, bd = to_dev(X, W, b)
+            Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+            got, p = _noalloc(h, Xd, Wd, bd, workloads.TAIL_NONE, Y)
+            assert p.split_k == 4 and p.schedule == 1
+            assert np.array_equal(got.astype(np.float64), oracle.linear_rows(X, W, b))
+
+
+def test_noalloc_rejects_problem_beyond_scratch():
+    """Tail (b) over 2^20 rows keeps 2^20 * tiles_n row maxima, more than the
+    64 MiB array for every tile shape: ETOOBIG before anything is enqueued
+    (Y keeps its canaries).  lin_epi_run, which may allocate, does it."""
+    M, N, K = 2**20, 8192, 4
+    X, W, b = workloads.make_inputs(M, N, K, seed=5)
+    Xd, Wd, bd = to_dev(X, W, b)
+    Y = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda:0")
+    with lib.LinEpi() as h:
+        rc = lib.lin_epi_run_noalloc(h.handle, M, N, K, Xd.data_ptr(), Wd.data_ptr(), bd.data_ptr(),
+                                     desc_for(workloads.TAIL_B), Y.data_ptr())
+        torch.cuda.synchronize()
+        assert rc == lib.LIN_EPI_ETOOBIG
+        assert torch.isnan(Y).all().item()
+        h.run_into(Xd, Wd, bd, desc_for(workloads.TAIL_B), Y)
+        torch.cuda.synchronize()
+    rows = np.array([0, 1, M // 2, M - 1])
+    compare(Y.cpu().numpy()[rows], oracle_rows(X, W, b, workloads.TAIL_B, rows), what="2^20-row tail b via run")
