@@ -103,6 +103,8 @@ def main() -> int:
     ap.add_argument("--workload", default="p1_2048x8192x8192", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--tail", type=int, default=None, help="tail index within the workload (default 0)")
     ap.add_argument("--split-k", type=int, default=0, help="0 auto, 1 off, S>=2 forced")
+    ap.add_argument("--tile", type=int, default=0, help="0 auto, else a tile configuration (LIN_EPI_OPT_TILE)")
+    ap.add_argument("--grid", type=int, default=0, help="0 auto, else a forced GEMM grid (LIN_EPI_OPT_GRID)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reg-staging", action="store_true",
@@ -145,6 +147,8 @@ def main() -> int:
     ref_tail = tail
     h = lib.LinEpi(stream=stream)
     h.set_option(lib.LIN_EPI_OPT_SPLIT_K, args.split_k)
+    h.set_option(lib.LIN_EPI_OPT_TILE, args.tile)
+    h.set_option(lib.LIN_EPI_OPT_GRID, args.grid)
     h.set_option(lib.LIN_EPI_OPT_UNFUSED, 1 if args.unfused else 0)
     h.set_option(lib.LIN_EPI_OPT_REG_STAGING, 1 if args.reg_staging else 0)
     flops = float(w.flops)
@@ -230,12 +234,24 @@ def main() -> int:
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = prof.total_ms[0] / max(1, prof.launches[0])
     traffic = measured_traffic(w.name)
+    # compulsory HBM bytes of one GEMM launch (X, W, b read once, the output
+    # written once) over its duration: the weight-streaming figure, reported
+    # for every workload beside whichever roofline bounds it
+    if args.pool_fold:
+        alg_bytes = 4.0 * (w.M * w.K + (w.N // 16) * (w.K + 1) + w.M)
+    else:
+        alg_bytes = float(w.algorithmic_bytes(tail))
+    # plus the partial sums of split tiles, each written once and read once
+    partial_bytes = 2.0 * plan.partial_bytes
+    hbm_gbs = (alg_bytes + partial_bytes) / (gemm_ms * 1e-3) / 1e9
+    hbm = {"achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": round(hbm_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": int(alg_bytes),
+           "partial_bytes": int(partial_bytes)}
     if w.bound == "hbm":
         # weight-streaming regime: algorithmic bytes per launch / launch time
-        alg_bytes = float(w.algorithmic_bytes(tail if not args.pool_fold else ref_tail))
-        roofline = {"bound": "hbm", "achieved": round(alg_bytes / (gemm_ms * 1e-3) / 1e9, 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-        roofline["frac"] = round(roofline["achieved"] / PEAK_HBM_GBS, 4)
+        alg_gbs = alg_bytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(alg_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(alg_gbs / PEAK_HBM_GBS, 4)}
     else:
         achieved = flops / (gemm_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
@@ -274,6 +290,7 @@ def main() -> int:
                         else "unfused" if args.unfused else "reg_staging" if args.reg_staging else "fused"),
         },
         "roofline": roofline,
+        "hbm": hbm,
         "parity_spot_check": {"rows": 4, "max_abs_err": spot_err, "ok": spot_ok},
     }
     if args.scale_fold:

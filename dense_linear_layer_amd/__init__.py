@@ -38,7 +38,10 @@ LIN_EPI_OPT_UNFUSED = 3
 LIN_EPI_OPT_TILE = 4
 LIN_EPI_OPT_REG_STAGING = 5
 LIN_EPI_OPT_GRID = 6
-TILE_CONFIGS = {1: (256, 256), 2: (128, 256), 3: (128, 128), 4: (64, 64), 5: (32, 128)}
+# tile option -> (tile_m, tile_n) the plan reports; 6 is the weight-streaming
+# kernel (16 rows of X against 64 rows of W per wavefront)
+TILE_CONFIGS = {1: (256, 256), 2: (128, 256), 3: (128, 128), 4: (64, 64), 5: (32, 128), 6: (16, 64)}
+TILE_DECODE = 6  # its K segments come from LIN_EPI_OPT_SPLIT_K; it has no stream-K grid
 
 # every function include/lin_epi.h declares
 EXPORTS = (
@@ -78,6 +81,7 @@ class lin_epi_plan(ctypes.Structure):
         ("kernels", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64),
         ("schedule", ctypes.c_int32),
+        ("partial_bytes", ctypes.c_int64),
     ]
 
 

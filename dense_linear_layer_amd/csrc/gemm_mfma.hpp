@@ -719,16 +719,19 @@ gemm_epi_kernel(GemmArgs a)
 }
 
 // Second pass of the row-max tails: Y[m] = max over column tiles of the
-// per-tile row maxima.  Max is exact, so the result does not depend on order.
+// per-tile row maxima, one wavefront per row (lanes take every 64th partial,
+// then a butterfly).  Max is exact, so the result does not depend on order.
 __global__ void __launch_bounds__(256) rowmax_finalize_kernel(const float *part, float *Y, int32_t M,
                                                               int32_t tiles_n)
 {
-    const int m = blockIdx.x * blockDim.x + threadIdx.x;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     if (m >= M) return;
     const float *p = part + (int64_t)m * tiles_n;
-    float v = p[0];
-    for (int t = 1; t < tiles_n; ++t) v = fmaxf(v, p[t]);
-    Y[m] = v;
+    float v = -INFINITY;
+    for (int t = lane; t < tiles_n; t += 64) v = fmaxf(v, p[t]);
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    if (lane == 0) Y[m] = v;
 }
 
 // ---------------------------------------------------------------------------

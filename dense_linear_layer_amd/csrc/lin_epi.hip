@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "gemm_mfma.hpp"
+#include "gemv_mfma.hpp"
 #include "lin_epi.h"
 
 using namespace lin_epi;
@@ -30,13 +31,24 @@ namespace {
 //           weight-streaming regime, where HBM rather than MFMA bounds);
 //           small workgroups so that two or more share a CU and keep enough
 //           weight bytes in flight
+//   DECODE  16x64 per wavefront, 4 independent wavefronts per workgroup, no
+//           LDS (gemv_mfma.hpp): operands streamed from HBM into a register
+//           ring; for M <= 16, where the layer is one read of W
 using CfgLarge = TileCfg<256, 256, 32, 4, 2, 1>;
 using CfgMid = TileCfg<128, 256, 32, 2, 4, 1>;
 using CfgSmall = TileCfg<128, 128, 32, 2, 2, 2>;
 using CfgTiny = TileCfg<64, 64, 32, 2, 2, 4>;
 using CfgSkinny = TileCfg<32, 128, 32, 1, 4, 4>;
 
-enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_COUNT = 5 };
+enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_DECODE = 5, CFG_COUNT = 6 };
+
+// The weight-streaming kernel: 16 rows of X against kGemvFN blocks of 16
+// rows of W per wavefront, a ring of kGemvDepth K steps of operands in
+// registers (64 W rows keep the X fragments, which every lane reloads from L2
+// each step, at a quarter of the weight bytes; 4 steps of 8 KiB in flight per
+// wavefront and one wavefront per SIMD streamed fastest on MI355X).
+constexpr int kGemvFN = 4;
+constexpr int kGemvDepth = 4;
 
 struct CfgInfo {
     int bm, bn, bk, wgs_per_cu;
@@ -49,6 +61,7 @@ constexpr CfgInfo kCfgs[CFG_COUNT] = {
     {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, 0.88},
     {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, 0.80},
     {CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, CfgSkinny::WG_PER_CU, 0.60},
+    {16, 16 * kGemvFN, kStepK, 4, 0.50},  // per wavefront; streams fastest with one wavefront per SIMD
 };
 static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
                   CfgMid::LDS_BYTES * CfgMid::WG_PER_CU <= 160 * 1024 &&
@@ -64,10 +77,11 @@ constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at
 constexpr double kRoundFixedS = 5e-6;           // per round of workgroups: first loads, epilogue, drain
 constexpr double kPassFixedS = 2e-6;            // one more kernel on the stream
 constexpr double kPassBytesPerS = 4e12;         // sustained HBM rate of partial-sum traffic
-constexpr double kGemmBytesPerS = 6.2e12;       // sustained HBM rate of a weight-streaming GEMM
+constexpr double kGemmBytesPerS = 5.9e12;       // sustained HBM rate of a weight-streaming MFMA tile kernel
 constexpr double kSingleStreamRate = 0.7;       // fraction of it with fewer than 2 workgroups per CU
 constexpr double kFixupFixedS = 3e-6;           // split tiles: release/acquire and the finishing reads
 constexpr double kCuBytesPerS = 60e9;           // one workgroup reading other segments' sums
+constexpr double kGemvBytesPerS = 6.1e12;       // weight-streaming kernel, one loading wavefront per SIMD
 
 struct PendingTiming {
     int role;
@@ -210,6 +224,10 @@ void launch_gemm(int cfg, bool multi, const GemmArgs &g, int64_t grid, hipStream
     }
 }
 
+struct Plan;
+template <int EPI>
+void launch_main(const Plan &pl, bool multi, const GemmArgs &g, hipStream_t s, bool reg_staging);
+
 bool is_rowmax(int kind)
 {
     return kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX || kind == LIN_EPI_GELU_SCALE_ROWMAX;
@@ -263,17 +281,28 @@ struct WsLayout {
     size_t counters, partials, rowmax, raw, total;  // byte offsets and size
 };
 
+// Floats in one partial-sum slot: the raw tile, or (tail (b) on the MFMA
+// tiles) its 16-column window sums; the weight-streaming kernel publishes
+// raw sums of its 16 x 16*FN block.
+int64_t slot_floats(const lin_epi_ctx *h, const Plan &pl, int kind)
+{
+    if (pl.cfg == CFG_DECODE) return 16 * 16 * kGemvFN;
+    return (int64_t)kCfgs[pl.cfg].bm * kCfgs[pl.cfg].bn /
+           (!h->unfused && kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);
+}
+
 WsLayout ws_layout(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, int kind)
 {
     WsLayout w{};
     const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
     const bool split = pl.segments > tiles;
-    const int64_t slot = (int64_t)kCfgs[pl.cfg].bm * kCfgs[pl.cfg].bn /
-                         (!h->unfused && kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);
+    const int64_t slot = slot_floats(h, pl, kind);
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
     w.counters = 0;
     w.partials = up((size_t)tiles * sizeof(int32_t));
-    const int64_t nslots = pl.schedule == 2 ? 2 * pl.grid : pl.grid;  // split-K never crosses a tile
+    // split-K never crosses a tile; a stream-K range ends in at most two
+    // split tiles; the weight-streaming kernel has one slot per wavefront
+    const int64_t nslots = pl.cfg == CFG_DECODE ? pl.segments : pl.schedule == 2 ? 2 * pl.grid : pl.grid;
     w.rowmax = w.partials + (split ? up((size_t)(nslots * slot) * sizeof(float)) : 0);
     const bool rm = is_rowmax(kind);
     w.raw = w.rowmax + (rm && !h->unfused ? up((size_t)(M * pl.tiles_n) * sizeof(float)) : 0);
@@ -308,9 +337,56 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
     bool any = false;
     const bool rowmax = is_rowmax(kind);
     const int steps = k_steps((int)K);
+    // A forced weight-streaming kernel the problem cannot use (rows of W
+    // spanning the buffer window) leaves the choice to the planner.
+    const bool decode_ok = (int64_t)16 * kGemvFN * K * 4 < kBufferWindow;
+    const int64_t tile_opt = h->tile_opt == CFG_DECODE + 1 && !decode_ok ? 0 : h->tile_opt;
     for (int c = 0; c < CFG_COUNT; ++c) {
         const CfgInfo &ci = kCfgs[c];
-        if (h->tile_opt > 0 && c != h->tile_opt - 1) continue;
+        if (tile_opt > 0 && c != tile_opt - 1) continue;
+        if (c == CFG_DECODE) {
+            // One wavefront per (X block, W block, K segment).  Time: reading
+            // W once per block of 16 X rows at the streaming rate, scaled
+            // down while there are fewer wavefronts than SIMDs, or the
+            // busiest SIMD's MFMA work if longer.  More wavefronts than SIMDs
+            // stream no faster; their extra segments only add partial sums.
+            const int64_t mblocks = (M + 15) / 16, wblocks = (N + ci.bn - 1) / ci.bn;
+            // W is read once per 16 rows of X: chosen automatically for at
+            // most two such blocks
+            if (!decode_ok || (tile_opt == 0 && mblocks > 2)) continue;
+            const int64_t blocks = mblocks * wblocks;
+            std::vector<int64_t> splits;
+            if (h->grid_opt > 0)
+                splits.push_back(std::max<int64_t>(1, std::min<int64_t>(h->grid_opt * kGemvWaves / blocks, steps)));
+            else if (h->split_opt == 1)
+                splits.push_back(1);
+            else if (h->split_opt >= 2)
+                splits.push_back(std::min<int64_t>(h->split_opt, steps));
+            else
+                for (int S = 1; S <= std::min(16, steps); ++S) splits.push_back(S);
+            const int64_t resident = 4 * (int64_t)num_cus;
+            for (int64_t S : splits) {
+                const int64_t units = blocks * S;
+                if (units > INT32_MAX) continue;
+                const double fill = std::min(1.0, (double)units / (double)resident);
+                const double t_hbm = 4.0 * ((double)mblocks * N * K + (double)M * K) / (kGemvBytesPerS * fill);
+                const int64_t per_simd = (units + 4 * (int64_t)num_cus - 1) / (4 * (int64_t)num_cus);
+                const double t_mfma = (double)per_simd * ((steps + S - 1) / S) * 8 * kGemvFN * 32 / (2.4e9 * ci.efficiency);
+                double t = std::max(t_hbm, t_mfma) + kRoundFixedS;
+                if (S > 1)
+                    t += kFixupFixedS + 2.0 * (double)(units - blocks) * 4 * 16 * ci.bn / kPassBytesPerS;
+                if (rowmax) t += kPassFixedS;
+                const Plan cand{c, (units + kGemvWaves - 1) / kGemvWaves, S > 1 ? 1 : 0, (int)S, units,
+                                (int)mblocks, (int)wblocks, steps};
+                if (max_ws != SIZE_MAX && (S > 1 || rowmax) && ws_layout(h, cand, M, N, kind).total > max_ws) continue;
+                if (t < best_t) {
+                    best_t = t;
+                    best = cand;
+                    any = true;
+                }
+            }
+            continue;
+        }
         const int64_t tm = (M + ci.bm - 1) / ci.bm, tn = (N + ci.bn - 1) / ci.bn;
         const int64_t tiles = tm * tn;
         const int64_t T = tiles * steps;
@@ -365,6 +441,20 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
     return best;
 }
 
+// The GEMM of a plan: the weight-streaming kernel or an MFMA tile kernel.
+template <int EPI>
+void launch_main(const Plan &pl, bool multi, const GemmArgs &g, hipStream_t s, bool reg_staging)
+{
+    if (pl.cfg == CFG_DECODE) {
+        const GemvArgs gv{g.X, g.W, g.bias,     g.out,   g.partials, g.counters, g.M, g.N,
+                          g.K, g.tiles_n, (int32_t)pl.segments, g.steps, g.koff, (int32_t)pl.max_seg, g.tail};
+        hipLaunchKernelGGL((gemv_mfma_kernel<EPI, kGemvFN, kGemvDepth>), dim3((unsigned)pl.grid),
+                           dim3(64 * kGemvWaves), 0, s, gv);
+        return;
+    }
+    launch_gemm<EPI>(pl.cfg, multi, g, pl.grid, s, reg_staging);
+}
+
 // The launch plan of one lin_epi_run call as the C interface reports it.
 //   fused:    GEMM with the tail in its epilogue (1 kernel); the row-max
 //             kinds add the finalize pass over per-tile row maxima
@@ -387,6 +477,7 @@ lin_epi_plan describe(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N
     const WsLayout w = ws_layout(h, pl, M, N, kind);
     const bool split = pl.segments > (int64_t)pl.tiles_m * pl.tiles_n;
     p.workspace_bytes = (split || is_rowmax(kind)) ? (int64_t)w.total : 0;
+    p.partial_bytes = split ? (pl.segments - (int64_t)pl.tiles_m * pl.tiles_n) * slot_floats(h, pl, kind) * 4 : 0;
     return p;
 }
 
@@ -622,26 +713,26 @@ int run_impl(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, 
         g.out = reinterpret_cast<float *>(ws + wl.rowmax);
         rc = timed_launch(h, 0, [&] {
             if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX)
-                launch_gemm<EPI_POOL_GELU_SCALE_ROWMAX>(pl.cfg, multi, g, pl.grid, s, h->reg_staging);
+                launch_main<EPI_POOL_GELU_SCALE_ROWMAX>(pl, multi, g, s, h->reg_staging);
             else
-                launch_gemm<EPI_GELU_SCALE_ROWMAX>(pl.cfg, multi, g, pl.grid, s, h->reg_staging);
+                launch_main<EPI_GELU_SCALE_ROWMAX>(pl, multi, g, s, h->reg_staging);
         });
         if (rc != LIN_EPI_OK) return rc;
         const float *part = g.out;
         const int32_t Mi = (int32_t)M, tn = (int32_t)pl.tiles_n;
         rc = timed_launch(h, 1, [&] {
-            hipLaunchKernelGGL(rowmax_finalize_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, part, Y, Mi, tn);
+            hipLaunchKernelGGL(rowmax_finalize_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, part, Y, Mi, tn);
         });
         if (rc != LIN_EPI_OK) return rc;
     } else if (!unfused) {
         g.out = Y;
         rc = timed_launch(h, 0, [&] {
             switch (kind) {
-                case LIN_EPI_NONE: launch_gemm<EPI_NONE>(pl.cfg, multi, g, pl.grid, s, h->reg_staging); break;
+                case LIN_EPI_NONE: launch_main<EPI_NONE>(pl, multi, g, s, h->reg_staging); break;
                 case LIN_EPI_SCALE_HARDTANH_GELU:
-                    launch_gemm<EPI_SCALE_HARDTANH_GELU>(pl.cfg, multi, g, pl.grid, s, h->reg_staging);
+                    launch_main<EPI_SCALE_HARDTANH_GELU>(pl, multi, g, s, h->reg_staging);
                     break;
-                default: launch_gemm<EPI_SWISH_SCALE>(pl.cfg, multi, g, pl.grid, s, h->reg_staging); break;
+                default: launch_main<EPI_SWISH_SCALE>(pl, multi, g, s, h->reg_staging); break;
             }
         });
         if (rc != LIN_EPI_OK) return rc;
@@ -651,7 +742,7 @@ int run_impl(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, 
         // tail as a separate pass.
         float *Yraw = rowmax ? reinterpret_cast<float *>(ws + wl.raw) : Y;
         g.out = Yraw;
-        rc = timed_launch(h, 0, [&] { launch_gemm<EPI_NONE>(pl.cfg, multi, g, pl.grid, s, h->reg_staging); });
+        rc = timed_launch(h, 0, [&] { launch_main<EPI_NONE>(pl, multi, g, s, h->reg_staging); });
         if (rc != LIN_EPI_OK) return rc;
         if (rowmax) {
             const int32_t pool = kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1;

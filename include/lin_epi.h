@@ -188,8 +188,11 @@ enum {
     LIN_EPI_OPT_UNFUSED = 3,
     /* Tile configuration: 0 = automatic (default); 1 = 256x256 tiles with 8
      * wavefronts, 2 = 128x256 with 8, 3 = 128x128 with 4, 4 = 64x64 with 4,
-     * 5 = 32x128 with 4 (few rows, weight streaming).
-     * The split-K choice is still made (or forced) as usual. */
+     * 5 = 32x128 with 4 (few rows, weight streaming), 6 = the weight-streaming
+     * kernel without LDS (16 rows of X against 64 rows of W per wavefront, any
+     * M; the plan reports a 16x64 tile; automatic when 64 rows of W span
+     * 1 GiB or more).  The split-K choice is still made (or forced) as
+     * usual. */
     LIN_EPI_OPT_TILE = 4,
     /* 1 = stage X and W tiles through registers (128-bit loads, then LDS
      * stores) even where the default direct-to-LDS buffer loads are usable;
@@ -217,6 +220,9 @@ typedef struct {
     int32_t schedule;               /* 0: one output tile per workgroup; 1: split-K, grid = tiles *
                                        split_k, equal K segments; 2: stream-K, workgroup ranges
                                        cross tile boundaries */
+    int64_t partial_bytes;          /* partial sums the split tiles' other segments publish for the
+                                       finishing one: one slot per such segment, each written once and
+                                       read back once (0 when no tile is split) */
 } lin_epi_plan;
 
 int lin_epi_last_plan(lin_epi_handle h, lin_epi_plan *out);

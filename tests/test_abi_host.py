@@ -109,9 +109,9 @@ def test_options_and_introspection_validation(handle):
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 2**31) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 300) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 0) == lib.LIN_EPI_OK
-    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 6) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 7) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, -1) == lib.LIN_EPI_EINVAL
-    for t in range(6):
+    for t in range(7):
         assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, t) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, 99, 0) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(0, lib.LIN_EPI_OPT_PROFILE, 1) == lib.LIN_EPI_EINVAL
@@ -173,7 +173,7 @@ def test_destroy_null_is_noop():
 
 def test_desc_layout_matches_header():
     assert ctypes.sizeof(lib.lin_epi_desc) == 24
-    assert ctypes.sizeof(lib.lin_epi_plan) == 48
+    assert ctypes.sizeof(lib.lin_epi_plan) == 56
     assert ctypes.sizeof(lib.lin_epi_profile) == 48
 
 
@@ -201,11 +201,12 @@ def test_planner_choices_for_the_workloads(handle):
     # every elementwise plan is one kernel; the ragged shape uses a split grid
     t = _plan(handle, 1000, 6000, 4100, A)
     assert t[3] == 1 and t[6] >= 1, t
-    # few rows against a long weight stream: 32x128 tiles, at least two
-    # workgroups per compute unit stream W
+    # few rows against a long weight stream: the weight-streaming kernel
+    # (16x64 per wavefront), with at least the 1024 wavefronts that give
+    # every SIMD one (256 workgroups of 4)
     for M in (1, 8, 16):
         t = _plan(handle, M, 32768, 32768, C)
-        assert t[:2] == (32, 128) and t[4] >= 512, t
+        assert t[:2] == (16, 64) and t[4] >= 256, t
 
 
 def test_planner_page2_never_writes_raw_partials(handle):
@@ -279,7 +280,10 @@ def test_planner_every_slice_gets_k(handle):
             assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, S) == 0
             tm, tn, s, _, grid, _, _ = _plan(handle, 300, 300, K, lib.LIN_EPI_NONE)
             assert 1 <= s <= max(1, -(-K // 32))
-            assert grid == -(-300 // tm) * -(-300 // tn) * s
+            # one workgroup per tile segment; the weight-streaming kernel
+            # (16x64) runs four wavefront units per workgroup
+            units = -(-300 // tm) * -(-300 // tn) * s
+            assert grid == (-(-units // 4) if (tm, tn) == (16, 64) else units)
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_SPLIT_K, 0) == 0
 
 

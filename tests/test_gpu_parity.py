@@ -225,7 +225,7 @@ def test_bound_stream_called_from_another_stream():
 # ------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("name", ["p1_2048x8192x8192", "p2_1024x8192x8192", "p3_128x32768x32768",
-                                  "p3_m16_16x32768x32768"])
+                                  "p3_m16_16x32768x32768", "p3_m8_8x32768x32768", "p3_m1_1x32768x32768"])
 def test_full_size_workload_checked_rows(h, name):
     """The large shapes at full size, in the launch configuration the benchmark
     times, checked on 64 seeded rows (all N outputs of each row)."""

@@ -29,7 +29,7 @@ def _name(request):
 
 
 @pytest.mark.parametrize("grid", [1, 5, 37, 256, 301, 512])
-@pytest.mark.parametrize("tile", sorted(lib.TILE_CONFIGS))
+@pytest.mark.parametrize("tile", sorted(t for t in lib.TILE_CONFIGS if t != lib.TILE_DECODE))
 def test_stream_k_integer_exact(tile, grid):
     """Forced stream-K grids on a shape ragged in M, N and K (K % 32 != 0,
     so the first K step of every tile is the partial one): bit-exact."""

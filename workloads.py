@@ -89,9 +89,12 @@ WORKLOADS = {
     "p2_1024x8192x8192": Workload("p2_1024x8192x8192", 1024, 8192, 8192, (TAIL_B,)),
     "p3_128x32768x32768": Workload("p3_128x32768x32768", 128, 32768, 32768, (TAIL_C,)),
     "ragged_1000x6000x4100": Workload("ragged_1000x6000x4100", 1000, 6000, 4100, (TAIL_A, TAIL_B, TAIL_C)),
-    # page l2_p59's layer with a decode-size batch: 16 rows against a 4 GiB
-    # weight, bounded by streaming W from HBM rather than by the matrix cores
+    # page l2_p59's layer with decode-size batches: 16, 8 and 1 rows against
+    # a 4 GiB weight, bounded by streaming W from HBM rather than by the
+    # matrix cores
     "p3_m16_16x32768x32768": Workload("p3_m16_16x32768x32768", 16, 32768, 32768, (TAIL_C,), bound="hbm"),
+    "p3_m8_8x32768x32768": Workload("p3_m8_8x32768x32768", 8, 32768, 32768, (TAIL_C,), bound="hbm"),
+    "p3_m1_1x32768x32768": Workload("p3_m1_1x32768x32768", 1, 32768, 32768, (TAIL_C,), bound="hbm"),
 }
 
 
