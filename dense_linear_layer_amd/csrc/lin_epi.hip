@@ -52,16 +52,17 @@ constexpr int kGemvDepth = 4;
 
 struct CfgInfo {
     int bm, bn, bk, wgs_per_cu;
+    int waves;          // wavefronts per workgroup
     double efficiency;  // fraction of the CU's 2.4 GHz fp32 MFMA peak, fitted to MI355X timings
 };
 
 constexpr CfgInfo kCfgs[CFG_COUNT] = {
-    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, 0.94},
-    {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, 0.90},
-    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, 0.88},
-    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, 0.80},
-    {CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, CfgSkinny::WG_PER_CU, 0.60},
-    {16, 16 * kGemvFN, kStepK, 4, 0.50},  // per wavefront; streams fastest with one wavefront per SIMD
+    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, CfgLarge::NW, 0.960},
+    {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, CfgMid::NW, 0.960},
+    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, CfgSmall::NW, 0.950},
+    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, CfgTiny::NW, 0.82},
+    {CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, CfgSkinny::WG_PER_CU, CfgSkinny::NW, 0.80},
+    {16, 16 * kGemvFN, kStepK, 4, 1, 0.50},  // per wavefront; streams fastest with one wavefront per SIMD
 };
 static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
                   CfgMid::LDS_BYTES * CfgMid::WG_PER_CU <= 160 * 1024 &&
@@ -71,10 +72,13 @@ static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
               "LDS budget");
 
 // Time-model constants of the planner, fitted (with the efficiencies above)
-// to timed (shape, tail, configuration, grid) combinations on MI355X, each
-// timed after enough warm-up for the engine clock to have ramped up.
+// to timed (shape, tail, configuration, grid) combinations on MI355X (18
+// shapes from 1x4096x4096 to 8192x8192x1024, every tile with split-K 1-16
+// and stream-K grids of 256-1024 workgroups), each timed after enough
+// warm-up for the engine clock to have ramped up.
 constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at the 2.4 GHz peak clock
 constexpr double kRoundFixedS = 5e-6;           // per round of workgroups: first loads, epilogue, drain
+constexpr double kThinRoundRate = 0.9;          // MFMA rate with fewer than two wavefronts per SIMD
 constexpr double kPassFixedS = 2e-6;            // one more kernel on the stream
 constexpr double kPassBytesPerS = 4e12;         // sustained HBM rate of partial-sum traffic
 constexpr double kGemmBytesPerS = 5.9e12;       // sustained HBM rate of a weight-streaming MFMA tile kernel
@@ -400,8 +404,12 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
             grids.push_back(tiles * std::min<int64_t>(h->split_opt, steps));
         } else {
             for (int S = 1; S <= std::min(16, steps); ++S) grids.push_back(tiles * S);
-            for (int64_t g : {slots, 2 * slots})
+            // stream-K within one round of resident workgroups (1..wgs_per_cu
+            // per CU): grids of several rounds measured markedly slower
+            for (int64_t k = 1; k <= ci.wgs_per_cu; ++k) {
+                const int64_t g = k * num_cus;
                 if (g > tiles && g < T && g % tiles != 0) grids.push_back(g);
+            }
         }
         const double slot_bytes = 4.0 * ci.bm * ci.bn / (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);
         // The 256x256 tile's accumulators leave no room for reading back
@@ -415,9 +423,14 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
             if (G != tiles && (T > INT32_MAX || G > INT32_MAX || !raw_split_ok)) G = tiles;
             const int64_t n_it = (T + G - 1) / G;
             const int64_t load = (G + num_cus - 1) / num_cus;
-            const double step_flops = 2.0 * ci.bm * ci.bn * kStepK;
-            double t = (double)((load + ci.wgs_per_cu - 1) / ci.wgs_per_cu) * kRoundFixedS +
-                       (double)load * n_it * step_flops / (kCuPeakFlops * ci.efficiency);
+            const double step_t = 2.0 * ci.bm * ci.bn * kStepK / (kCuPeakFlops * ci.efficiency);
+            // the busiest CU runs its workgroups wgs_per_cu at a time; a round
+            // that leaves fewer than two wavefronts per SIMD runs slower
+            auto rate = [&](int64_t k) { return k * ci.waves < 8 ? kThinRoundRate : 1.0; };
+            const int64_t full = load / ci.wgs_per_cu, rem = load % ci.wgs_per_cu;
+            double t = (double)(full + (rem ? 1 : 0)) * kRoundFixedS +
+                       (double)(full * ci.wgs_per_cu) * n_it * step_t / rate(ci.wgs_per_cu) +
+                       (rem ? (double)rem * n_it * step_t / rate(rem) : 0.0);
             double t_hbm = 4.0 * ((double)N * K + (double)M * K) / kGemmBytesPerS;
             if (G < 2 * (int64_t)num_cus) t_hbm /= kSingleStreamRate;
             t = std::max(t, t_hbm);

@@ -321,3 +321,31 @@ def test_noalloc_validation_before_any_hip_call(handle, args, expect):
     a.update(args)
     rc = lib.lin_epi_run_noalloc(a["h"], a["M"], a["N"], a["K"], a["X"], a["W"], a["b"], a["desc"], a["Y"])
     assert rc == expect, lib.lin_epi_status_string(rc)
+
+
+def test_planner_fitted_choices(handle):
+    """Plans the fitted time model picks where MI355X timings of every
+    candidate plan put them best (or within 1.5 % of it)."""
+    A, B = lib.LIN_EPI_SCALE_HARDTANH_GELU, lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX
+    # tail (b) at 1024x8192x8192: 128x256 tiles, one per compute unit, no split
+    assert _plan(handle, 1024, 8192, 8192, B)[:5] == (128, 256, 1, 2, 256)
+    # the ragged layer: 128x128 tiles, stream-K over one round of two
+    # workgroups per compute unit
+    for kind in (A, B):
+        tm, tn, s, k, grid, ws, sched = _plan(handle, 1000, 6000, 4100, kind)
+        assert (tm, tn, grid, sched) == (128, 128, 512, 2)
+    # many mid-sized tiles: 64x64, one per workgroup
+    assert _plan(handle, 3000, 3000, 3000, A)[:5] == (64, 64, 1, 1, 47 * 47)
+    assert _plan(handle, 512, 4096, 4096, A)[:5] == (64, 64, 1, 1, 512)
+
+
+def test_planner_stream_k_stays_within_one_round(handle):
+    """Stream-K grids of more than one round of resident workgroups measured
+    markedly slower, so the planner never picks one."""
+    per_cu = {(256, 256): 1, (128, 256): 1, (128, 128): 2, (64, 64): 4, (32, 128): 4}
+    for M, N, K in [(1000, 6000, 4100), (3000, 3000, 3000), (768, 3072, 3072), (300, 530, 1028),
+                    (2000, 2000, 8192), (257, 513, 100), (4096, 100, 50000)]:
+        for kind in range(5):
+            tm, tn, s, k, grid, ws, sched = _plan(handle, M, N, K, kind)
+            if sched == 2:
+                assert grid <= 256 * per_cu[(tm, tn)], (M, N, K, kind, tm, tn, grid)
