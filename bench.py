@@ -39,7 +39,7 @@ PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak (256 CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_linear_layer_amd", "csrc", f) for f in
-                  ("gemm_mfma.hpp", "epilogue.hpp", "lin_epi.hip")]
+                  ("gemm_mfma.hpp", "gemv_mfma.hpp", "epilogue.hpp", "dma_layout.hpp", "schedule.hpp", "lin_epi.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -55,15 +55,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs,
-    or None when they were taken on different kernel sources."""
+def measured_traffic(workload: str, tail: str, variant: str):
+    """HBM bytes per launch of the main kernel from the committed rocprofv3
+    counter runs (keyed "workload:tail:variant"), or None when they were
+    taken on different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = t.get(workload)
+    entry = t.get("%s:%s:%s" % (workload, tail, variant))
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
@@ -233,7 +234,9 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = prof.total_ms[0] / max(1, prof.launches[0])
-    traffic = measured_traffic(w.name)
+    variant = ("pool_fold" if args.pool_fold else "scale_fold" if args.scale_fold
+               else "unfused" if args.unfused else "reg_staging" if args.reg_staging else "fused")
+    traffic = measured_traffic(w.name, ref_tail.name, variant)
     # compulsory HBM bytes of one GEMM launch (X, W, b read once, the output
     # written once) over its duration: the weight-streaming figure, reported
     # for every workload beside whichever roofline bounds it
@@ -286,8 +289,7 @@ def main() -> int:
             "split_k": plan.split_k,
             "kernels_per_step": plan.kernels,
             "frac_of_fp32_mfma_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
-            "variant": ("pool_fold" if args.pool_fold else "scale_fold" if args.scale_fold
-                        else "unfused" if args.unfused else "reg_staging" if args.reg_staging else "fused"),
+            "variant": variant,
         },
         "roofline": roofline,
         "hbm": hbm,
