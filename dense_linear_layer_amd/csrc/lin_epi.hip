@@ -57,10 +57,10 @@ struct CfgInfo {
 };
 
 constexpr CfgInfo kCfgs[CFG_COUNT] = {
-    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, CfgLarge::NW, 0.960},
-    {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, CfgMid::NW, 0.960},
+    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, CfgLarge::NW, 0.965},
+    {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, CfgMid::NW, 0.970},
     {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, CfgSmall::NW, 0.950},
-    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, CfgTiny::NW, 0.82},
+    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, CfgTiny::NW, 0.88},
     {CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, CfgSkinny::WG_PER_CU, CfgSkinny::NW, 0.80},
     {16, 16 * kGemvFN, kStepK, 4, 1, 0.50},  // per wavefront; streams fastest with one wavefront per SIMD
 };
@@ -79,6 +79,7 @@ static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
 constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at the 2.4 GHz peak clock
 constexpr double kRoundFixedS = 5e-6;           // per round of workgroups: first loads, epilogue, drain
 constexpr double kThinRoundRate = 0.9;          // MFMA rate with fewer than two wavefronts per SIMD
+constexpr double kStreamKRate = 0.95;           // stream-K ranges start at scattered K positions: little L2 reuse
 constexpr double kPassFixedS = 2e-6;            // one more kernel on the stream
 constexpr double kPassBytesPerS = 4e12;         // sustained HBM rate of partial-sum traffic
 constexpr double kGemmBytesPerS = 5.9e12;       // sustained HBM rate of a weight-streaming MFMA tile kernel
@@ -428,9 +429,10 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
             // that leaves fewer than two wavefronts per SIMD runs slower
             auto rate = [&](int64_t k) { return k * ci.waves < 8 ? kThinRoundRate : 1.0; };
             const int64_t full = load / ci.wgs_per_cu, rem = load % ci.wgs_per_cu;
+            const double sk = (G != tiles && G % tiles != 0) ? kStreamKRate : 1.0;
             double t = (double)(full + (rem ? 1 : 0)) * kRoundFixedS +
-                       (double)(full * ci.wgs_per_cu) * n_it * step_t / rate(ci.wgs_per_cu) +
-                       (rem ? (double)rem * n_it * step_t / rate(rem) : 0.0);
+                       ((double)(full * ci.wgs_per_cu) * n_it * step_t / rate(ci.wgs_per_cu) +
+                        (rem ? (double)rem * n_it * step_t / rate(rem) : 0.0)) / sk;
             double t_hbm = 4.0 * ((double)N * K + (double)M * K) / kGemmBytesPerS;
             if (G < 2 * (int64_t)num_cus) t_hbm /= kSingleStreamRate;
             t = std::max(t, t_hbm);
