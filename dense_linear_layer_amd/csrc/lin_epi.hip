@@ -26,6 +26,7 @@ namespace {
 //   MID    128x256, 8 wavefronts (2x4, 64x64 each),   96 KiB LDS, 1 WG/CU
 //   SMALL  128x128, 4 wavefronts (2x2, 64x64 each),   64 KiB LDS, 2 WG/CU
 //   TINY    64x64,  4 wavefronts (2x2, 32x32 each),   32 KiB LDS, 4 WG/CU
+//   WIDE    64x128, 4 wavefronts (2x2, 32x64 each),  48 KiB LDS, 3 WG/CU
 //   SKINNY  32x128, 4 wavefronts (1x4, 32x32 each),  40 KiB LDS, 4 WG/CU:
 //           few rows of X against a long stream of W rows (the small-M,
 //           weight-streaming regime, where HBM rather than MFMA bounds);
@@ -39,8 +40,11 @@ using CfgMid = TileCfg<128, 256, 32, 2, 4, 1>;
 using CfgSmall = TileCfg<128, 128, 32, 2, 2, 2>;
 using CfgTiny = TileCfg<64, 64, 32, 2, 2, 4>;
 using CfgSkinny = TileCfg<32, 128, 32, 1, 4, 4>;
+using CfgWide = TileCfg<64, 128, 32, 2, 2, 3>;
 
-enum CfgId { CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_DECODE = 5, CFG_COUNT = 6 };
+enum CfgId {
+    CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_DECODE = 5, CFG_WIDE = 6, CFG_COUNT = 7
+};
 
 // The weight-streaming kernel: 16 rows of X against kGemvFN blocks of 16
 // rows of W per wavefront, a ring of kGemvDepth K steps of operands in
@@ -57,28 +61,30 @@ struct CfgInfo {
 };
 
 constexpr CfgInfo kCfgs[CFG_COUNT] = {
-    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, CfgLarge::NW, 0.965},
+    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, CfgLarge::NW, 0.970},
     {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, CfgMid::NW, 0.970},
-    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, CfgSmall::NW, 0.950},
-    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, CfgTiny::NW, 0.88},
+    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, CfgSmall::NW, 0.960},
+    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, CfgTiny::NW, 0.865},
     {CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, CfgSkinny::WG_PER_CU, CfgSkinny::NW, 0.80},
     {16, 16 * kGemvFN, kStepK, 4, 1, 0.50},  // per wavefront; streams fastest with one wavefront per SIMD
+    {CfgWide::BM, CfgWide::BN, CfgWide::BK, CfgWide::WG_PER_CU, CfgWide::NW, 0.920},
 };
 static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
                   CfgMid::LDS_BYTES * CfgMid::WG_PER_CU <= 160 * 1024 &&
                   CfgSmall::LDS_BYTES * CfgSmall::WG_PER_CU <= 160 * 1024 &&
                   CfgTiny::LDS_BYTES * CfgTiny::WG_PER_CU <= 160 * 1024 &&
-                  CfgSkinny::LDS_BYTES * CfgSkinny::WG_PER_CU <= 160 * 1024,
+                  CfgSkinny::LDS_BYTES * CfgSkinny::WG_PER_CU <= 160 * 1024 &&
+                  CfgWide::LDS_BYTES * CfgWide::WG_PER_CU <= 160 * 1024,
               "LDS budget");
 
 // Time-model constants of the planner, fitted (with the efficiencies above)
-// to timed (shape, tail, configuration, grid) combinations on MI355X (18
+// to timed (shape, tail, configuration, grid) combinations on MI355X (22
 // shapes from 1x4096x4096 to 8192x8192x1024, every tile with split-K 1-16
 // and stream-K grids of 256-1024 workgroups), each timed after enough
 // warm-up for the engine clock to have ramped up.
 constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at the 2.4 GHz peak clock
 constexpr double kRoundFixedS = 5e-6;           // per round of workgroups: first loads, epilogue, drain
-constexpr double kThinRoundRate = 0.9;          // MFMA rate with fewer than two wavefronts per SIMD
+constexpr double kThinRoundRate = 0.95;         // MFMA rate with fewer than two wavefronts per SIMD
 constexpr double kStreamKRate = 0.95;           // stream-K ranges start at scattered K positions: little L2 reuse
 constexpr double kPassFixedS = 2e-6;            // one more kernel on the stream
 constexpr double kPassBytesPerS = 4e12;         // sustained HBM rate of partial-sum traffic
@@ -225,7 +231,9 @@ void launch_gemm(int cfg, bool multi, const GemmArgs &g, int64_t grid, hipStream
         case CFG_TINY * 2: launch_gemm_cfg<CfgTiny, EPI, false>(g, grid, s, reg_staging); break;
         case CFG_TINY * 2 + 1: launch_gemm_cfg<CfgTiny, EPI, true>(g, grid, s, reg_staging); break;
         case CFG_SKINNY * 2: launch_gemm_cfg<CfgSkinny, EPI, false>(g, grid, s, reg_staging); break;
-        default: launch_gemm_cfg<CfgSkinny, EPI, true>(g, grid, s, reg_staging); break;
+        case CFG_SKINNY * 2 + 1: launch_gemm_cfg<CfgSkinny, EPI, true>(g, grid, s, reg_staging); break;
+        case CFG_WIDE * 2: launch_gemm_cfg<CfgWide, EPI, false>(g, grid, s, reg_staging); break;
+        default: launch_gemm_cfg<CfgWide, EPI, true>(g, grid, s, reg_staging); break;
     }
 }
 
@@ -395,7 +403,6 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
         const int64_t tm = (M + ci.bm - 1) / ci.bm, tn = (N + ci.bn - 1) / ci.bn;
         const int64_t tiles = tm * tn;
         const int64_t T = tiles * steps;
-        const int64_t slots = num_cus * (int64_t)ci.wgs_per_cu;
         std::vector<int64_t> grids;
         if (h->grid_opt > 0) {
             grids.push_back(std::min<int64_t>(h->grid_opt, T));
@@ -406,10 +413,11 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
         } else {
             for (int S = 1; S <= std::min(16, steps); ++S) grids.push_back(tiles * S);
             // stream-K within one round of resident workgroups (1..wgs_per_cu
-            // per CU): grids of several rounds measured markedly slower
+            // per CU, fewer or more workgroups than tiles): grids of several
+            // rounds measured markedly slower
             for (int64_t k = 1; k <= ci.wgs_per_cu; ++k) {
                 const int64_t g = k * num_cus;
-                if (g > tiles && g < T && g % tiles != 0) grids.push_back(g);
+                if (g != tiles && g < T && g % tiles != 0) grids.push_back(g);
             }
         }
         const double slot_bytes = 4.0 * ci.bm * ci.bn / (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);

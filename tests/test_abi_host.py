@@ -109,9 +109,9 @@ def test_options_and_introspection_validation(handle):
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 2**31) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 300) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_GRID, 0) == lib.LIN_EPI_OK
-    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 7) == lib.LIN_EPI_EINVAL
+    assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, 8) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, -1) == lib.LIN_EPI_EINVAL
-    for t in range(7):
+    for t in range(8):
         assert lib.lin_epi_set_option(handle, lib.LIN_EPI_OPT_TILE, t) == lib.LIN_EPI_OK
     assert lib.lin_epi_set_option(handle, 99, 0) == lib.LIN_EPI_EINVAL
     assert lib.lin_epi_set_option(0, lib.LIN_EPI_OPT_PROFILE, 1) == lib.LIN_EPI_EINVAL
@@ -188,9 +188,9 @@ def _plan(handle, M, N, K, kind, cus=256):
 def test_planner_choices_for_the_workloads(handle):
     A, B, C, F = (lib.LIN_EPI_SCALE_HARDTANH_GELU, lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX, lib.LIN_EPI_SWISH_SCALE,
                   lib.LIN_EPI_GELU_SCALE_ROWMAX)
-    # 2048x8192x8192: 128x256 tiles, two rounds of one per compute unit, no
-    # split, no workspace (measured 0.4 % ahead of 256x256 tiles, one round)
-    assert _plan(handle, 2048, 8192, 8192, A) == (128, 256, 1, 1, 512, 0, 0)
+    # 2048x8192x8192: 256x256 tiles, one per compute unit, no split, no
+    # workspace (128x256 tiles in two rounds measure level with it)
+    assert _plan(handle, 2048, 8192, 8192, A) == (256, 256, 1, 1, 256, 0, 0)
     # 128x32768x32768: 128x256 tiles (128 of them) split in two, finished in
     # the GEMM kernel itself (one kernel)
     assert _plan(handle, 128, 32768, 32768, C)[:5] == (128, 256, 2, 1, 256)
@@ -331,23 +331,21 @@ def test_planner_fitted_choices(handle):
     A, B = lib.LIN_EPI_SCALE_HARDTANH_GELU, lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX
     # tail (b) at 1024x8192x8192: 128x256 tiles, one per compute unit, no split
     assert _plan(handle, 1024, 8192, 8192, B)[:5] == (128, 256, 1, 2, 256)
-    # the ragged layer: tail (b) on 128x128 tiles, stream-K over one round of
-    # two workgroups per compute unit (pooled partial sums); the elementwise
-    # tails on 64x64 tiles, one per workgroup (no raw partial sums, every
-    # workgroup of a round starting at the same K position)
-    tm, tn, s, k, grid, ws, sched = _plan(handle, 1000, 6000, 4100, B)
-    assert (tm, tn, grid, sched) == (128, 128, 512, 2)
-    for kind in (A, lib.LIN_EPI_SWISH_SCALE):
-        assert _plan(handle, 1000, 6000, 4100, kind)[:5] == (64, 64, 1, 1, 16 * 94)
-    # many mid-sized tiles: 64x64, one per workgroup
-    assert _plan(handle, 3000, 3000, 3000, A)[:5] == (64, 64, 1, 1, 47 * 47)
-    assert _plan(handle, 512, 4096, 4096, A)[:5] == (64, 64, 1, 1, 512)
+    # the ragged layer, every tail: 64x128 tiles, one per workgroup, 752 of
+    # them in one round of three workgroups per compute unit (no partial
+    # sums, every workgroup starting at the same K position)
+    for kind in (A, B, lib.LIN_EPI_SWISH_SCALE):
+        assert _plan(handle, 1000, 6000, 4100, kind)[:5] == (64, 128, 1, 1 + (kind == B), 16 * 47)
+    # 512x4096x4096: 256 tiles of 64x128, one per compute unit
+    assert _plan(handle, 512, 4096, 4096, A)[:5] == (64, 128, 1, 1, 256)
+    # 3000x3000x3000: 128x256 tiles, stream-K over 256 workgroups (288 tiles)
+    assert _plan(handle, 3000, 3000, 3000, A)[:5] == (128, 256, 2, 1, 256)
 
 
 def test_planner_stream_k_stays_within_one_round(handle):
     """Stream-K grids of more than one round of resident workgroups measured
     markedly slower, so the planner never picks one."""
-    per_cu = {(256, 256): 1, (128, 256): 1, (128, 128): 2, (64, 64): 4, (32, 128): 4}
+    per_cu = {(256, 256): 1, (128, 256): 1, (128, 128): 2, (64, 64): 4, (32, 128): 4, (64, 128): 3}
     for M, N, K in [(1000, 6000, 4100), (3000, 3000, 3000), (768, 3072, 3072), (300, 530, 1028),
                     (2000, 2000, 8192), (257, 513, 100), (4096, 100, 50000)]:
         for kind in range(5):
