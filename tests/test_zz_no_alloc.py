@@ -69,6 +69,11 @@ SEQUENCES = {
         (1000, 6000, 4100, workloads.TAIL_B, dict()),
         (128, 1024, 8192, workloads.TAIL_C, dict()),
     ],
+    "weight_streaming_then_smaller": [
+        (8, 4096, 4100, workloads.TAIL_C, dict(split=5, tile=6)),
+        (3, 200, 36, workloads.TAIL_B, dict(split=2, tile=6)),
+        (16, 2000, 1028, workloads.TAIL_A, dict()),
+    ],
 }
 
 
