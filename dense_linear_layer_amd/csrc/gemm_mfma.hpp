@@ -72,6 +72,12 @@ struct GemmArgs {
     float *out;         // Y [M,N]; or row-max partials [M, tiles_n]
     float *partials;    // partial-sum slots of split tiles (2 per workgroup)
     int32_t *counters;  // per-tile arrival counters, zero before and after every launch
+    // Row-max tails: when Y is set, the last workgroup of each tile row to
+    // finish takes the max over that row's per-tile partials (in `out`) and
+    // writes Y [M]; rowcnt holds one arrival counter per tile row, zero
+    // before and after every launch.  When Y is null a separate pass does it.
+    float *Y;
+    int32_t *rowcnt;
     int32_t M, N, K;
     int32_t tiles_m, tiles_n;
     int32_t steps;  // K steps per tile (k_steps(K))
@@ -621,6 +627,46 @@ gemm_epi_kernel(GemmArgs a)
             }
         }
 
+        // Row-max tails: this tile's row maxima (cross-wavefront partials in
+        // red[WAVES_N][BM]) go to the per-(row, tile) partials; then, when the
+        // kernel finishes the rows itself, the last of the tile row's
+        // workgroups to arrive (device-scope counter, as for split tiles)
+        // takes the max over the row's partials, one wavefront per row, lanes
+        // over the tiles.  Partials travel with device-scope cache policy.
+        auto publish_row_max = [&](const float *red) {
+            constexpr int kDeviceScope = 16;  // cache-policy bit sc1
+            const int rows = min(BM, M - m0);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                a.out + (int64_t)m0 * a.tiles_n, (short)0, rows * a.tiles_n * 4, 0x00020000);
+            __syncthreads();
+            for (int r = tid; r < rows; r += NT) {
+                float x = red[r];
+#pragma unroll
+                for (int w = 1; w < WAVES_N; ++w) x = fmaxf(x, red[w * BM + r]);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, (r * a.tiles_n + tn) * 4, 0,
+                                                      kDeviceScope);
+            }
+            if (!a.Y) return;
+            wait_vmcnt<0>();
+            __syncthreads();  // red is read: its first word can hold the flag
+            int &s_row_last = *reinterpret_cast<int *>(smem);
+            if (tid == 0)
+                s_row_last = __hip_atomic_fetch_add(a.rowcnt + tm, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                             a.tiles_n - 1;
+            __syncthreads();
+            if (!s_row_last) return;
+            if (tid == 0) __hip_atomic_store(a.rowcnt + tm, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int r = wave_u; r < rows; r += NW) {
+                float v = -INFINITY;
+                for (int t = lane; t < a.tiles_n; t += 64)
+                    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                rs, (r * a.tiles_n + t) * 4, 0, kDeviceScope)));
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+                if (lane == 0) a.Y[m0 + r] = v;
+            }
+        };
+
         if (finish) {
             if constexpr (POOL) {
                 // Row maximum of scale * GELU(window mean) over this tile's
@@ -643,16 +689,7 @@ gemm_epi_kernel(GemmArgs a)
                     mx = fmaxf(mx, __shfl_xor(mx, 16));
                     if (!(qw & 1)) red[wn * BM + wm * TM + i * 32 + 8 * (u >> 2) + 4 * (qw >> 1) + (u & 3)] = mx;
                 }
-                __syncthreads();
-                for (int r = tid; r < BM; r += NT) {
-                    const int m = m0 + r;
-                    if (m < M) {
-                        float x = red[r];
-#pragma unroll
-                        for (int w = 1; w < WAVES_N; ++w) x = fmaxf(x, red[w * BM + r]);
-                        a.out[(int64_t)m * a.tiles_n + tn] = x;
-                    }
-                }
+                publish_row_max(red);
             } else if constexpr (ROWMAX) {
                 // Row maximum of scale * GELU(y) over this tile's columns (the
                 // pooled-weight form, whose columns already are window means).
@@ -683,16 +720,7 @@ gemm_epi_kernel(GemmArgs a)
                         mx = fmaxf(mx, __shfl_xor(mx, 16));
                         if ((lane & 31) == 0) red[wn * BM + wm * TM + i * 32 + (r >> 2) * 8 + row_half + (r & 3)] = mx;
                     }
-                __syncthreads();
-                for (int r = tid; r < BM; r += NT) {
-                    const int m = m0 + r;
-                    if (m < M) {
-                        float x = red[r];
-#pragma unroll
-                        for (int w = 1; w < WAVES_N; ++w) x = fmaxf(x, red[w * BM + r]);
-                        a.out[(int64_t)m * a.tiles_n + tn] = x;
-                    }
-                }
+                publish_row_max(red);
             } else {
                 using Tail = typename std::conditional<
                     EPI == EPI_SCALE_HARDTANH_GELU, TailScaleHardtanhGelu,

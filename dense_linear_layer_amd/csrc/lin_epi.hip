@@ -286,7 +286,8 @@ struct Plan {
     int steps;
 };
 
-// Workspace layout of one run: [arrival counters, one int per tile, rounded
+// Workspace layout of one run: [arrival counters, one int per tile, then
+// one per tile row for a row-max tail finished in the tile kernel, rounded
 // up to 256 bytes][partial-sum slots when tiles are split: one per
 // workgroup for split-K, two for stream-K][row-max partials M * tiles_n]
 // [raw linear output M * N: unfused row-max tails only].
@@ -304,6 +305,13 @@ int64_t slot_floats(const lin_epi_ctx *h, const Plan &pl, int kind)
            (!h->unfused && kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX ? 16 : 1);
 }
 
+// The fused row-max tails on the MFMA tiles finish the row maxima in the
+// GEMM kernel itself (the weight-streaming kernel leaves them to a pass).
+bool rowmax_in_kernel(const lin_epi_ctx *h, const Plan &pl, int kind)
+{
+    return is_rowmax(kind) && !h->unfused && pl.cfg != CFG_DECODE;
+}
+
 WsLayout ws_layout(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, int kind)
 {
     WsLayout w{};
@@ -312,7 +320,8 @@ WsLayout ws_layout(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, i
     const int64_t slot = slot_floats(h, pl, kind);
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
     w.counters = 0;
-    w.partials = up((size_t)tiles * sizeof(int32_t));
+    const int64_t row_counters = rowmax_in_kernel(h, pl, kind) ? pl.tiles_m : 0;
+    w.partials = up((size_t)(tiles + row_counters) * sizeof(int32_t));
     // split-K never crosses a tile; a stream-K range ends in at most two
     // split tiles; the weight-streaming kernel has one slot per wavefront
     const int64_t nslots = pl.cfg == CFG_DECODE ? pl.segments : pl.schedule == 2 ? 2 * pl.grid : pl.grid;
@@ -448,7 +457,8 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
             if (st.segments > tiles)
                 t += kFixupFixedS + 2.0 * (double)(st.segments - tiles) * slot_bytes / kPassBytesPerS +
                      (st.max_per_tile - 1) * slot_bytes / kCuBytesPerS;
-            if (rowmax) t += kPassFixedS;
+            // (row-max tails: the tile kernel's last workgroup of each tile
+            // row finishes the row, no second pass)
             const Plan cand{c, G, G == tiles ? 0 : G % tiles == 0 ? 1 : 2, st.max_per_tile, st.segments,
                             (int)tm, (int)tn, steps};
             if (max_ws != SIZE_MAX && (st.segments > tiles || rowmax) && ws_layout(h, cand, M, N, kind).total > max_ws)
@@ -496,7 +506,7 @@ lin_epi_plan describe(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N
     if (h->unfused)
         p.kernels = 1 + (kind != LIN_EPI_NONE ? 1 : 0);
     else
-        p.kernels = is_rowmax(kind) ? 2 : 1;
+        p.kernels = is_rowmax(kind) && !rowmax_in_kernel(h, pl, kind) ? 2 : 1;
     const WsLayout w = ws_layout(h, pl, M, N, kind);
     const bool split = pl.segments > (int64_t)pl.tiles_m * pl.tiles_n;
     p.workspace_bytes = (split || is_rowmax(kind)) ? (int64_t)w.total : 0;
@@ -683,6 +693,8 @@ int run_impl(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, 
     const WsLayout wl = ws_layout(h, pl, M, N, kind);
     const bool split = pl.segments > tiles;  // some tile is cut into K segments
     const bool multi = pl.grid != tiles;     // workgroups walk ranges (segment-loop kernel)
+    const bool row_fin = rowmax_in_kernel(h, pl, kind);
+    const bool counters = split || row_fin;  // arrival counters in use, zero before the launch
     hipStream_t s = h->stream;
 
     GemmArgs g{};
@@ -704,7 +716,7 @@ int run_impl(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, 
     char *ws = nullptr;
     if ((split || rowmax) && fixed) {
         ws = fixed->base;
-        if (split) {
+        if (counters) {
             // the fixed array keeps whatever the last call left: clear the
             // arrival counters (a fill kernel, not a memset)
             const int64_t n = (int64_t)(wl.partials / sizeof(int32_t));
@@ -718,7 +730,7 @@ int run_impl(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, 
         rc = ensure_workspace(h, wl.total);
         if (rc != LIN_EPI_OK) return rc;
         ws = static_cast<char *>(h->ws);
-        if (split && wl.partials > h->ws_clean) {
+        if (counters && wl.partials > h->ws_clean) {
             // arrival counters start at zero (and every run leaves them so)
             const int64_t n = (int64_t)(wl.partials / sizeof(int32_t));
             const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
@@ -732,8 +744,13 @@ int run_impl(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, 
 
     if (!unfused && rowmax) {
         // GEMM with the row-max epilogue -> per-(row, column tile) partials ->
-        // max over column tiles.
+        // max over column tiles: by the tile kernel's last workgroup of each
+        // tile row, or (weight-streaming kernel) by a second pass.
         g.out = reinterpret_cast<float *>(ws + wl.rowmax);
+        if (row_fin) {
+            g.Y = Y;
+            g.rowcnt = reinterpret_cast<int32_t *>(ws + wl.counters) + tiles;
+        }
         rc = timed_launch(h, 0, [&] {
             if (kind == LIN_EPI_POOL_GELU_SCALE_ROWMAX)
                 launch_main<EPI_POOL_GELU_SCALE_ROWMAX>(pl, multi, g, s, h->reg_staging);
@@ -741,12 +758,15 @@ int run_impl(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const float *X, 
                 launch_main<EPI_GELU_SCALE_ROWMAX>(pl, multi, g, s, h->reg_staging);
         });
         if (rc != LIN_EPI_OK) return rc;
-        const float *part = g.out;
-        const int32_t Mi = (int32_t)M, tn = (int32_t)pl.tiles_n;
-        rc = timed_launch(h, 1, [&] {
-            hipLaunchKernelGGL(rowmax_finalize_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, part, Y, Mi, tn);
-        });
-        if (rc != LIN_EPI_OK) return rc;
+        if (!row_fin) {
+            const float *part = g.out;
+            const int32_t Mi = (int32_t)M, tn = (int32_t)pl.tiles_n;
+            rc = timed_launch(h, 1, [&] {
+                hipLaunchKernelGGL(rowmax_finalize_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, part, Y, Mi,
+                                   tn);
+            });
+            if (rc != LIN_EPI_OK) return rc;
+        }
     } else if (!unfused) {
         g.out = Y;
         rc = timed_launch(h, 0, [&] {

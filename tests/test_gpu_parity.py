@@ -144,10 +144,11 @@ def test_forced_split_k(tail, S):
         Xd, Wd, bd = to_dev(X, W, b)
         got = run_gpu(h, Xd, Wd, bd, tail)
         p = h.plan()
-        # the last workgroup of each tile adds the K segments in the GEMM
-        # kernel itself; only the row-max tails add their finalize pass
+        # the last workgroup of each tile adds the K segments, and for the
+        # row-max tails the last of each tile row takes the row maximum, in
+        # the GEMM kernel itself
         assert p.split_k == S and p.schedule == 1
-        assert p.kernels == (2 if tail.kind in (workloads.POOL_GELU_SCALE_ROWMAX, workloads.GELU_SCALE_ROWMAX) else 1)
+        assert p.kernels == 1
         compare(got, oracle_rows(X, W, b, tail), what="split-K %d %s" % (S, tail.name))
         again = [run_gpu(h, Xd, Wd, bd, tail) for _ in range(2)]
         for a in again:

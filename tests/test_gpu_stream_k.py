@@ -60,7 +60,7 @@ def test_stream_k_all_tails_deterministic(tail, tile, grid):
         h.set_option(lib.LIN_EPI_OPT_GRID, grid)
         got = run_gpu(h, Xd, Wd, bd, tail)
         p = h.plan()
-        assert p.kernels == (2 if tail.kind in ROWMAX else 1)
+        assert p.kernels == 1  # row maxima too are finished in the tile kernel
         compare(got, oracle_rows(X, W, b, tail), what="stream-K tile %d grid %d %s" % (tile, grid, tail.name))
         for _ in range(2):
             assert np.array_equal(run_gpu(h, Xd, Wd, bd, tail), got), "stream-K rerun not bitwise identical"
@@ -154,3 +154,36 @@ def test_random_stream_k_matches_oracle(M, N, K, tail, tile, grid):
         p = h.plan()
     compare(got, oracle_rows(X, W, b, tail), what="%dx%dx%d %s tile %dx%d grid %d" % (M, N, K, tail.name, p.tile_m,
                                                                                       p.tile_n, p.grid_main))
+
+
+def test_row_max_finish_across_shapes_one_handle():
+    """The row-max tails finish in the tile kernel: the last workgroup of
+    each tile row to arrive (one device-scope counter per tile row, after the
+    per-tile counters in the workspace) takes the max over the row's per-tile
+    partials.  One handle, so one workspace, runs shapes whose tile-row and
+    column-tile counts grow and shrink (more than 64 column tiles, where a
+    lane takes several; a single one), whole-tile and stream-K; each result
+    matches the oracle and reruns bitwise, so every run left its counters
+    at zero."""
+    cases = [
+        (300, 5000, 260, workloads.TAIL_B, 4, 0),        # 5 x 79 tiles of 64x64
+        (1000, 300, 516, workloads.TAIL_B_FOLDED, 5, 0),  # 32 x 3 tiles of 32x128
+        (70, 16, 36, workloads.TAIL_B, 3, 0),             # one column tile
+        (300, 5000, 260, workloads.TAIL_B, 4, 301),      # stream-K, 79 column tiles
+        (513, 2100, 1028, workloads.TAIL_B_FOLDED, 7, 0),
+        (129, 4100, 300, workloads.TAIL_B, 0, 0),         # the planner's choice
+        (300, 5000, 260, workloads.TAIL_B, 4, 0),
+    ]
+    with lib.LinEpi() as h:
+        for M, N, K, tail, tile, grid in cases:
+            log("case %dx%dx%d %s tile %d grid %d" % (M, N, K, tail.name, tile, grid))
+            X, W, b = workloads.make_inputs(M, N, K, seed=M + N + K + grid)
+            Xd, Wd, bd = to_dev(X, W, b)
+            h.set_option(lib.LIN_EPI_OPT_TILE, tile)
+            h.set_option(lib.LIN_EPI_OPT_GRID, grid)
+            got = run_gpu(h, Xd, Wd, bd, tail)
+            p = h.plan()
+            assert p.kernels == 1 and (p.tile_m, p.tile_n) != lib.TILE_CONFIGS[lib.TILE_DECODE]
+            compare(got, oracle_rows(X, W, b, tail), what="%dx%dx%d %s tile %dx%d grid %d" % (
+                M, N, K, tail.name, p.tile_m, p.tile_n, p.grid_main))
+            assert np.array_equal(run_gpu(h, Xd, Wd, bd, tail), got), "rerun not bitwise identical"
