@@ -215,7 +215,8 @@ typedef struct {
     int32_t tile_m, tile_n, tile_k; /* workgroup output tile and K step */
     int32_t split_k;                /* most K segments any output tile is cut into (1 = none) */
     int64_t grid_main;              /* workgroups of the GEMM kernel */
-    int32_t kernels;                /* kernels launched (GEMM + row-max finalize or unfused tail) */
+    int32_t kernels;                /* kernels launched: 1, or 2 with the row-max finalize pass (behind
+                                       the weight-streaming kernel only) or the unfused tail kernel */
     int64_t workspace_bytes;        /* workspace the run used */
     int32_t schedule;               /* 0: one output tile per workgroup; 1: split-K, grid = tiles *
                                        split_k, equal K segments; 2: stream-K, workgroup ranges
@@ -237,7 +238,7 @@ int lin_epi_query_plan(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const 
 
 /* Accumulated kernel timings since the last read (profiling on).  Waits for
  * the handle's stream.  Role 0 is the GEMM kernel, role 1 the second pass
- * (row-max finalize), role 2 the separate tail kernel of the unfused
+ * (row-max finalize behind the weight-streaming kernel), role 2 the separate tail kernel of the unfused
  * ablation, lin_epi_pool_weights and lin_epi_scale_weights. */
 typedef struct {
     int64_t launches[3];
