@@ -746,8 +746,9 @@ gemm_epi_kernel(GemmArgs a)
     } while (SPLIT && it < it_end);
 }
 
-// Second pass of the row-max tails: Y[m] = max over column tiles of the
-// per-tile row maxima, one wavefront per row (lanes take every 64th partial,
+// Second pass of the row-max tails behind the weight-streaming kernel (the
+// tile kernel finishes its rows itself): Y[m] = max over column blocks of the
+// per-block row maxima, one wavefront per row (lanes take every 64th partial,
 // then a butterfly).  Max is exact, so the result does not depend on order.
 __global__ void __launch_bounds__(256) rowmax_finalize_kernel(const float *part, float *Y, int32_t M,
                                                               int32_t tiles_n)
