@@ -632,19 +632,19 @@ gemm_epi_kernel(GemmArgs a)
         // kernel finishes the rows itself, the last of the tile row's
         // workgroups to arrive (device-scope counter, as for split tiles)
         // takes the max over the row's partials, one wavefront per row, lanes
-        // over the tiles.  Partials travel with device-scope cache policy.
+        // over the tiles.  The partials are written and read back with
+        // relaxed device-scope atomics (plain loads and stores with
+        // device-scope cache policy), 64-bit addressed.
         auto publish_row_max = [&](const float *red) {
-            constexpr int kDeviceScope = 16;  // cache-policy bit sc1
             const int rows = min(BM, M - m0);
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                a.out + (int64_t)m0 * a.tiles_n, (short)0, rows * a.tiles_n * 4, 0x00020000);
+            uint32_t *const part = reinterpret_cast<uint32_t *>(a.out + (int64_t)m0 * a.tiles_n);
             __syncthreads();
             for (int r = tid; r < rows; r += NT) {
                 float x = red[r];
 #pragma unroll
                 for (int w = 1; w < WAVES_N; ++w) x = fmaxf(x, red[w * BM + r]);
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, (r * a.tiles_n + tn) * 4, 0,
-                                                      kDeviceScope);
+                __hip_atomic_store(part + (int64_t)r * a.tiles_n + tn, __builtin_bit_cast(uint32_t, x), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
             if (!a.Y) return;
             wait_vmcnt<0>();
@@ -657,10 +657,11 @@ gemm_epi_kernel(GemmArgs a)
             if (!s_row_last) return;
             if (tid == 0) __hip_atomic_store(a.rowcnt + tm, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int r = wave_u; r < rows; r += NW) {
+                const uint32_t *pr = part + (int64_t)r * a.tiles_n;
                 float v = -INFINITY;
                 for (int t = lane; t < a.tiles_n; t += 64)
-                    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                                rs, (r * a.tiles_n + t) * 4, 0, kDeviceScope)));
+                    v = fmaxf(v, __builtin_bit_cast(float, __hip_atomic_load(pr + t, __ATOMIC_RELAXED,
+                                                                             __HIP_MEMORY_SCOPE_AGENT)));
 #pragma unroll
                 for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
                 if (lane == 0) a.Y[m0 + r] = v;

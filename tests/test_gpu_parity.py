@@ -344,6 +344,29 @@ def test_output_beyond_2_to_31_elements(tail):
     compare(got, oracle_rows(X, W, b, tail, rows), what="M*N > 2^31, %s" % tail.name)
 
 
+def test_row_max_partials_beyond_2_gib_per_tile_row():
+    """Tail (b) on 256x256 tiles with 2^21 + 1 column tiles: one tile row's
+    per-tile row maxima (256 rows x 2^21 + 1 tiles x 4 bytes) span more than
+    2^31 bytes, so the tile kernel's partial stores and its last workgroup's
+    read-back must use 64-bit offsets.  W is 8.6 GB (K = 4)."""
+    M, N, K = 257, 2**29 + 48, 4
+    tail = workloads.TAIL_B
+    assert 256 * -(-N // 256) * 4 > 2**31
+    X, W, b = workloads.make_inputs(M, N, K, seed=29)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        h.set_option(lib.LIN_EPI_OPT_TILE, 1)
+        h.set_option(lib.LIN_EPI_OPT_SPLIT_K, 1)
+        got = run_gpu(h, Xd, Wd, bd, tail)
+        p = h.plan()
+        assert (p.tile_m, p.tile_n, p.kernels) == (256, 256, 1)
+    del Xd, Wd, bd
+    torch.cuda.empty_cache()
+    # row 255's partials of the last column tiles lie past byte 2^31
+    rows = np.array([0, 255, 256])
+    compare(got[rows], oracle_rows(X, W, b, tail, rows), what="row-max partials > 2 GiB per tile row")
+
+
 @pytest.mark.parametrize("K", [2**20 - 4, 2**20])
 @pytest.mark.parametrize("split", [1, 3])
 def test_long_k_across_the_buffer_window(K, split):
