@@ -1,6 +1,6 @@
 // C ABI of the fused fp32 linear layer (include/lin_epi.h): argument
 // validation, kernel selection, workspace management and optional per-kernel
-// timing.  Kernels live in gemm_mfma.hpp and epilogue.hpp.
+// timing.  Kernels live in gemm_mfma.hpp, gemv_mfma.hpp and epilogue.hpp.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -16,10 +16,10 @@ using namespace lin_epi;
 
 namespace {
 
-// Tile table.  All use v_mfma_f32_32x32x2_f32 and two LDS stages; they
-// differ in workgroup tile and wavefront count, and the dispatcher picks one
-// per call (choose_plan below).  All stage 32-deep K steps with
-// direct-to-LDS buffer loads (LDS figures below; rows padded to 36 floats,
+// Tile table.  The LDS tiles use v_mfma_f32_32x32x2_f32 and two LDS stages;
+// they differ in workgroup tile and wavefront count, and the dispatcher picks
+// one configuration per call (choose_plan below).  They stage 32-deep K
+// steps with direct-to-LDS buffer loads (LDS figures below; rows padded to 36 floats,
 // 12 % more, on the register-staged path used when a tile's rows of X or W
 // span 1 GiB or more):
 //   LARGE  256x256, 8 wavefronts (4x2, 64x128 each), 128 KiB LDS, 1 WG/CU
