@@ -238,8 +238,9 @@ int lin_epi_query_plan(lin_epi_handle h, int64_t M, int64_t N, int64_t K, const 
 
 /* Accumulated kernel timings since the last read (profiling on).  Waits for
  * the handle's stream.  Role 0 is the GEMM kernel, role 1 the second pass
- * (row-max finalize behind the weight-streaming kernel), role 2 the separate tail kernel of the unfused
- * ablation, lin_epi_pool_weights and lin_epi_scale_weights. */
+ * (row-max finalize behind the weight-streaming kernel), role 2 the separate
+ * tail kernel of the unfused ablation, lin_epi_pool_weights and
+ * lin_epi_scale_weights. */
 typedef struct {
     int64_t launches[3];
     double total_ms[3];
