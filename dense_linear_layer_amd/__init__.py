@@ -40,7 +40,7 @@ LIN_EPI_OPT_REG_STAGING = 5
 LIN_EPI_OPT_GRID = 6
 # tile option -> (tile_m, tile_n) the plan reports; 6 is the weight-streaming
 # kernel (16 rows of X against 64 rows of W per wavefront)
-TILE_CONFIGS = {1: (256, 256), 2: (128, 256), 3: (128, 128), 4: (64, 64), 5: (32, 128), 6: (16, 64), 7: (64, 128)}
+TILE_CONFIGS = {1: (256, 256), 2: (128, 256), 3: (128, 128), 4: (64, 64), 5: (32, 128), 6: (16, 64), 7: (64, 128), 8: (128, 96)}
 TILE_DECODE = 6  # its K segments come from LIN_EPI_OPT_SPLIT_K; it has no stream-K grid
 
 # every function include/lin_epi.h declares

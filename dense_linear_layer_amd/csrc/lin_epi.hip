@@ -27,6 +27,9 @@ namespace {
 //   SMALL  128x128, 4 wavefronts (2x2, 64x64 each),   64 KiB LDS, 2 WG/CU
 //   TINY    64x64,  4 wavefronts (2x2, 32x32 each),   32 KiB LDS, 4 WG/CU
 //   WIDE    64x128, 4 wavefronts (2x2, 32x64 each),  48 KiB LDS, 3 WG/CU
+//   TALL   128x96,  4 wavefronts (4x1, 32x96 each),  56 KiB LDS, 2 WG/CU:
+//           a quarter fewer fragment reads per MFMA than WIDE, for shapes
+//           whose 128x96 tiles fill rounds of two per CU
 //   SKINNY  32x128, 4 wavefronts (1x4, 32x32 each),  40 KiB LDS, 4 WG/CU:
 //           few rows of X against a long stream of W rows (the small-M,
 //           weight-streaming regime, where HBM rather than MFMA bounds);
@@ -41,9 +44,11 @@ using CfgSmall = TileCfg<128, 128, 32, 2, 2, 2>;
 using CfgTiny = TileCfg<64, 64, 32, 2, 2, 4>;
 using CfgSkinny = TileCfg<32, 128, 32, 1, 4, 4>;
 using CfgWide = TileCfg<64, 128, 32, 2, 2, 3>;
+using CfgTall = TileCfg<128, 96, 32, 4, 1, 2>;
 
 enum CfgId {
-    CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_DECODE = 5, CFG_WIDE = 6, CFG_COUNT = 7
+    CFG_LARGE = 0, CFG_MID = 1, CFG_SMALL = 2, CFG_TINY = 3, CFG_SKINNY = 4, CFG_DECODE = 5, CFG_WIDE = 6, CFG_TALL = 7,
+    CFG_COUNT = 8
 };
 
 // The weight-streaming kernel: 16 rows of X against kGemvFN blocks of 16
@@ -58,23 +63,30 @@ struct CfgInfo {
     int bm, bn, bk, wgs_per_cu;
     int waves;          // wavefronts per workgroup
     double efficiency;  // fraction of the CU's 2.4 GHz fp32 MFMA peak, fitted to MI355X timings
+    double thin_rate;   // relative MFMA rate of a round with fewer than two wavefronts per SIMD
 };
 
 constexpr CfgInfo kCfgs[CFG_COUNT] = {
-    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, CfgLarge::NW, 0.970},
-    {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, CfgMid::NW, 0.970},
-    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, CfgSmall::NW, 0.960},
-    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, CfgTiny::NW, 0.865},
-    {CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, CfgSkinny::WG_PER_CU, CfgSkinny::NW, 0.80},
-    {16, 16 * kGemvFN, kStepK, 4, 1, 0.50},  // per wavefront; streams fastest with one wavefront per SIMD
-    {CfgWide::BM, CfgWide::BN, CfgWide::BK, CfgWide::WG_PER_CU, CfgWide::NW, 0.920},
+    {CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, CfgLarge::WG_PER_CU, CfgLarge::NW, 0.975, 0.95},
+    {CfgMid::BM, CfgMid::BN, CfgMid::BK, CfgMid::WG_PER_CU, CfgMid::NW, 0.975, 0.95},
+    {CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::WG_PER_CU, CfgSmall::NW, 0.960, 0.95},
+    {CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, CfgTiny::WG_PER_CU, CfgTiny::NW, 0.895, 0.95},
+    {CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, CfgSkinny::WG_PER_CU, CfgSkinny::NW, 0.895, 0.95},
+    {16, 16 * kGemvFN, kStepK, 4, 1, 0.50, 1.0},  // per wavefront; streams fastest with one wavefront per SIMD
+    {CfgWide::BM, CfgWide::BN, CfgWide::BK, CfgWide::WG_PER_CU, CfgWide::NW, 0.950, 0.95},
+    // a hair under WIDE: on the shapes both fill (1000x6000x4100) they time
+    // within +-2 % of each other box to box; measured at full rate with one
+    // workgroup per CU (stream-K on 768x3072x3072, 1536x1536x6144,
+    // 640x5000x5000), unlike the other tiles
+    {CfgTall::BM, CfgTall::BN, CfgTall::BK, CfgTall::WG_PER_CU, CfgTall::NW, 0.949, 1.0},
 };
 static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
                   CfgMid::LDS_BYTES * CfgMid::WG_PER_CU <= 160 * 1024 &&
                   CfgSmall::LDS_BYTES * CfgSmall::WG_PER_CU <= 160 * 1024 &&
                   CfgTiny::LDS_BYTES * CfgTiny::WG_PER_CU <= 160 * 1024 &&
                   CfgSkinny::LDS_BYTES * CfgSkinny::WG_PER_CU <= 160 * 1024 &&
-                  CfgWide::LDS_BYTES * CfgWide::WG_PER_CU <= 160 * 1024,
+                  CfgWide::LDS_BYTES * CfgWide::WG_PER_CU <= 160 * 1024 &&
+                  CfgTall::LDS_BYTES * CfgTall::WG_PER_CU <= 160 * 1024,
               "LDS budget");
 
 // Time-model constants of the planner, fitted (with the efficiencies above)
@@ -84,7 +96,6 @@ static_assert(CfgLarge::LDS_BYTES * CfgLarge::WG_PER_CU <= 160 * 1024 &&
 // warm-up for the engine clock to have ramped up.
 constexpr double kCuPeakFlops = 256.0 * 2.4e9;  // fp32 MFMA FLOP/s of one CU at the 2.4 GHz peak clock
 constexpr double kRoundFixedS = 5e-6;           // per round of workgroups: first loads, epilogue, drain
-constexpr double kThinRoundRate = 0.95;         // MFMA rate with fewer than two wavefronts per SIMD
 constexpr double kStreamKRate = 0.95;           // stream-K ranges start at scattered K positions: little L2 reuse
 constexpr double kPassFixedS = 2e-6;            // one more kernel on the stream
 constexpr double kPassBytesPerS = 4e12;         // sustained HBM rate of partial-sum traffic
@@ -233,7 +244,9 @@ void launch_gemm(int cfg, bool multi, const GemmArgs &g, int64_t grid, hipStream
         case CFG_SKINNY * 2: launch_gemm_cfg<CfgSkinny, EPI, false>(g, grid, s, reg_staging); break;
         case CFG_SKINNY * 2 + 1: launch_gemm_cfg<CfgSkinny, EPI, true>(g, grid, s, reg_staging); break;
         case CFG_WIDE * 2: launch_gemm_cfg<CfgWide, EPI, false>(g, grid, s, reg_staging); break;
-        default: launch_gemm_cfg<CfgWide, EPI, true>(g, grid, s, reg_staging); break;
+        case CFG_WIDE * 2 + 1: launch_gemm_cfg<CfgWide, EPI, true>(g, grid, s, reg_staging); break;
+        case CFG_TALL * 2: launch_gemm_cfg<CfgTall, EPI, false>(g, grid, s, reg_staging); break;
+        default: launch_gemm_cfg<CfgTall, EPI, true>(g, grid, s, reg_staging); break;
     }
 }
 
@@ -343,7 +356,8 @@ WsLayout ws_layout(const lin_epi_ctx *h, const Plan &pl, int64_t M, int64_t N, i
 //   longer when fewer than two workgroups per CU stream); split tiles add
 //     t_fix = t_fix0 + (published sums, written and read) / HBM rate
 //           + (max segments - 1) * slot / one workgroup's read rate
-//   and the row-max tails one finalize kernel.
+//   and the row-max tails behind the weight-streaming kernel one finalize
+//   kernel.
 // Padding waste is included (a tile's work counts in full).  The fastest
 // estimate wins.  LIN_EPI_OPT_SPLIT_K = 1 forbids splitting, S >= 2 forces
 // S segments per tile (clamped to the K steps available);
@@ -444,7 +458,7 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
             const double step_t = 2.0 * ci.bm * ci.bn * kStepK / (kCuPeakFlops * ci.efficiency);
             // the busiest CU runs its workgroups wgs_per_cu at a time; a round
             // that leaves fewer than two wavefronts per SIMD runs slower
-            auto rate = [&](int64_t k) { return k * ci.waves < 8 ? kThinRoundRate : 1.0; };
+            auto rate = [&](int64_t k) { return k * ci.waves < 8 ? ci.thin_rate : 1.0; };
             const int64_t full = load / ci.wgs_per_cu, rem = load % ci.wgs_per_cu;
             const double sk = (G != tiles && G % tiles != 0) ? kStreamKRate : 1.0;
             double t = (double)(full + (rem ? 1 : 0)) * kRoundFixedS +

@@ -192,7 +192,8 @@ enum {
      * kernel without LDS (16 rows of X against 64 rows of W per wavefront, any
      * M; the plan reports a 16x64 tile; automatic when 64 rows of W span
      * 1 GiB or more), 7 = 64x128 with 4 wavefronts (three workgroups per
-     * CU).  The split-K choice is still made (or forced) as usual. */
+     * CU), 8 = 128x96 with 4 wavefronts (two workgroups per CU).  The
+     * split-K choice is still made (or forced) as usual. */
     LIN_EPI_OPT_TILE = 4,
     /* 1 = stage X and W tiles through registers (128-bit loads, then LDS
      * stores) even where the default direct-to-LDS buffer loads are usable;

@@ -187,3 +187,23 @@ def test_row_max_finish_across_shapes_one_handle():
             compare(got, oracle_rows(X, W, b, tail), what="%dx%dx%d %s tile %dx%d grid %d" % (
                 M, N, K, tail.name, p.tile_m, p.tile_n, p.grid_main))
             assert np.array_equal(run_gpu(h, Xd, Wd, bd, tail), got), "rerun not bitwise identical"
+
+
+@pytest.mark.parametrize("M,N,K,tail", [(3000, 3000, 3000, workloads.TAIL_A), (768, 3072, 3072, workloads.TAIL_C),
+                                        (1536, 1536, 6144, workloads.TAIL_A), (640, 5000, 5000, workloads.TAIL_C)],
+                         ids=["3000^3-a", "768x3072x3072-c", "1536x1536x6144-a", "640x5000x5000-c"])
+def test_planner_choice_on_128x96_shapes(M, N, K, tail):
+    """Shapes where the planner picks the 128x96 tile (a round and a half of
+    whole tiles at 3000^3; stream-K over one workgroup per CU for the others):
+    64 sampled rows against the oracle, and a bitwise rerun."""
+    X, W, b = workloads.make_inputs(M, N, K, seed=M + K)
+    Xd, Wd, bd = to_dev(X, W, b)
+    with lib.LinEpi() as h:
+        got = run_gpu(h, Xd, Wd, bd, tail)
+        p = h.plan()
+        log("plan: tile %dx%d grid %d schedule %d segments %d" % (p.tile_m, p.tile_n, p.grid_main, p.schedule,
+                                                                 p.split_k))
+        assert (p.tile_m, p.tile_n) == (128, 96)
+        assert np.array_equal(run_gpu(h, Xd, Wd, bd, tail), got), "rerun not bitwise identical"
+    rows = workloads.checked_rows(M, seed=M)
+    compare(got[rows], oracle_rows(X, W, b, tail, rows), what="%dx%dx%d %s" % (M, N, K, tail.name))

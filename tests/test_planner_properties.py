@@ -16,7 +16,7 @@ import dense_linear_layer_amd as lib
 
 ROWMAX = (lib.LIN_EPI_POOL_GELU_SCALE_ROWMAX, lib.LIN_EPI_GELU_SCALE_ROWMAX)
 # resident workgroups per CU of each LDS tile
-PER_CU = {(256, 256): 1, (128, 256): 1, (128, 128): 2, (64, 64): 4, (32, 128): 4, (64, 128): 3}
+PER_CU = {(256, 256): 1, (128, 256): 1, (128, 128): 2, (64, 64): 4, (32, 128): 4, (64, 128): 3, (128, 96): 2}
 DECODE = lib.TILE_CONFIGS[lib.TILE_DECODE]
 CUS = 256
 
