@@ -457,7 +457,8 @@ Plan choose_plan(const lin_epi_ctx *h, int64_t M, int64_t N, int64_t K, int kind
             const int64_t load = (G + num_cus - 1) / num_cus;
             const double step_t = 2.0 * ci.bm * ci.bn * kStepK / (kCuPeakFlops * ci.efficiency);
             // the busiest CU runs its workgroups wgs_per_cu at a time; a round
-            // that leaves fewer than two wavefronts per SIMD runs slower
+            // that leaves fewer than two wavefronts per SIMD runs at the
+            // tile's thin_rate
             auto rate = [&](int64_t k) { return k * ci.waves < 8 ? ci.thin_rate : 1.0; };
             const int64_t full = load / ci.wgs_per_cu, rem = load % ci.wgs_per_cu;
             const double sk = (G != tiles && G % tiles != 0) ? kStreamKRate : 1.0;
