@@ -95,6 +95,9 @@ WORKLOADS = {
     "p3_m16_16x32768x32768": Workload("p3_m16_16x32768x32768", 16, 32768, 32768, (TAIL_C,), bound="hbm"),
     "p3_m8_8x32768x32768": Workload("p3_m8_8x32768x32768", 8, 32768, 32768, (TAIL_C,), bound="hbm"),
     "p3_m1_1x32768x32768": Workload("p3_m1_1x32768x32768", 1, 32768, 32768, (TAIL_C,), bound="hbm"),
+    # not one of the pages' layers: a square shape whose tiles do not fill
+    # whole rounds, where the planner picks the 128x96 tile (timed for it)
+    "square_3000x3000x3000": Workload("square_3000x3000x3000", 3000, 3000, 3000, (TAIL_A,)),
 }
 
 
