@@ -344,6 +344,10 @@ def test_planner_fitted_choices(handle):
     assert _plan(handle, 3000, 3000, 3000, A)[:5] == (128, 96, 1, 1, 768)
     # 2000x2000x8192: 512 tiles of 64x128, no split
     assert _plan(handle, 2000, 2000, 8192, A)[:5] == (64, 128, 1, 1, 512)
+    # 96 rows: not the 32-row tile (kept for 17-32 rows; at 96 rows it timed
+    # 25 % behind the best plan), the 128x96 tile split in two instead
+    assert _plan(handle, 96, 12288, 12288, lib.LIN_EPI_SWISH_SCALE)[:5] == (128, 96, 2, 1, 256)
+    assert _plan(handle, 32, 16384, 16384, lib.LIN_EPI_SWISH_SCALE)[:2] == (32, 128)
     # 768x3072x3072, 1536x1536x6144, 640x5000x5000: 128x96 stream-K over 256
     # workgroups, one per compute unit (192, 192 and 260 tiles)
     for M, N, K in ((768, 3072, 3072), (1536, 1536, 6144), (640, 5000, 5000)):
